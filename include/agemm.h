@@ -1,0 +1,132 @@
+/*
+ * agemm.h — flag-gated, shard-decomposed AG+GEMM on one MI355X (gfx950).
+ *
+ * The operation (source: "Eliminating Multi-GPU Performance Taxes", detailed
+ * analysis page — symbol table and the AG+GEMM core identity):
+ *
+ *     C = A . B = [A_0 | A_1 | ... | A_{W-1}] . B
+ *       = sum_{s=0}^{W-1} A_s . B[s*K/W : (s+1)*K/W, :]
+ *
+ * A (M x K) is split along K into W shards A_s (M x K/W); B (K x N) and C
+ * (M x N) are whole. In the page's Push model a producer stores every shard
+ * into a receive buffer Inbox(s, k) and then raises a ready counter
+ * Flags(s, k) per tile; the GEMM waits on each tile's flag and consumes that
+ * K-slice at once instead of waiting for the whole all-gather. The page's
+ * ordering requirement (its correctness check #4) is that a consumer which
+ * sees the flag raised also sees the data. Here all W inbox slots live in the
+ * HBM of one GPU and the ordering is an agent-scope release (producer) /
+ * acquire (consumer) pair.
+ *
+ * Layouts: every matrix is row-major fp16 (IEEE binary16) unless stated.
+ *   A_s   M x KS, KS = K/W, row stride KS elements (one buffer per shard)
+ *   B     K x N,  row stride N (N contiguous); shard s uses rows [s*KS, (s+1)*KS)
+ *   C     M x N,  row stride N; fp16 (rounded to nearest even from the fp32
+ *         accumulator) or fp32, chosen at create time; overwritten (no beta)
+ * A k-tile is BKf consecutive columns of one shard over all M rows;
+ * tile id = s*KT + kt with KT = KS/BKf, T = W*KT tiles in all.
+ *
+ * Shapes accepted: 1 <= W <= 16, K % W == 0, KS % 64 == 0, N % 8 == 0,
+ * N >= 8, 1 <= M <= 2^31-1, BKf a multiple of 64 that divides KS, T <= 64.
+ * Pointers: device pointers, 16-byte aligned. Streams are hipStream_t passed
+ * as void* (NULL = the null stream).
+ *
+ * Errors: every call returns an agemm_status and never aborts. Arguments are
+ * validated before anything is launched; a rejected call changes no state.
+ * Calls are asynchronous on the given stream. A consumer that waits longer
+ * than the spin timeout for a flag stops, records the tile in a device error
+ * word and leaves C undefined; agemm_check() reports it after the caller has
+ * synchronised.
+ *
+ * Ownership: the context owns the inbox (W x M x KS fp16), the flags (T
+ * uint32 counters), the gathered-A buffer of the BSP path, the split-K
+ * workspace and the error word. The caller owns A_s, B, C and all streams.
+ * A context is not thread-safe; use one per host thread.
+ */
+#ifndef AGEMM_H
+#define AGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct agemm_ctx agemm_ctx;
+
+typedef enum {
+  AGEMM_OK = 0,
+  AGEMM_EINVAL = 1,   /* null or misaligned pointer, bad enum, bad schedule */
+  AGEMM_ESHAPE = 2,   /* shape outside the accepted set above */
+  AGEMM_ENOMEM = 3,   /* device or host allocation failed */
+  AGEMM_EHIP = 4,     /* a HIP runtime call failed; see agemm_last_error */
+  AGEMM_ETIMEOUT = 5, /* a consumer gave up waiting for a flag (reported by agemm_check) */
+  AGEMM_ESTATE = 6    /* call out of order, e.g. run_fused before any produce */
+} agemm_status;
+
+typedef enum { AGEMM_F16 = 0, AGEMM_F32 = 1 } agemm_dtype;
+
+/* Release schedule of the producer (host arrays, read during the call only).
+ * order[p] is the tile id released p-th; offset_ns[p] is its release time in
+ * nanoseconds after the producer starts, non-decreasing in p. n must equal T
+ * and order must be a permutation of 0..T-1. */
+typedef struct {
+  int32_t n;
+  const int32_t* order;
+  const int64_t* offset_ns;
+} agemm_schedule;
+
+/* Creates a context for one shape. flag_ktile = BKf in elements; 0 picks
+ * min(256, KS), widened until T <= 64. Allocates the inbox and the flags
+ * (zeroed) on the current device. */
+int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype,
+                 int64_t flag_ktile);
+
+/* Frees everything the context owns. Synchronises the device first. NULL is accepted. */
+int agemm_destroy(agemm_ctx* ctx);
+
+/* Shape queries: BKf, KT = KS/BKf and T = W*KT (any output pointer may be NULL). */
+int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
+
+/* Producer (Push model): copies tile (s, kt) of A_s into Inbox(s) and then
+ * raises Flags(s, kt), for every tile, in the schedule's order and at its
+ * times (sched == NULL: shard order, no delay). a_shards: host array of W
+ * device pointers, each M x KS fp16. Starts a new epoch: the next run_fused
+ * waits for this call's flags. Before it overwrites the inbox, the producer
+ * stream waits (device side) for the last run_fused on the previous epoch. */
+int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_schedule* sched, void* stream);
+
+/* Flag-gated consumer: C = sum_s Inbox(s) . B_s, waiting on Flags(s, kt)
+ * before reading each k-tile. Meant to run concurrently with agemm_produce
+ * on another stream. B: K x N fp16; C: M x N in the context's dtype. */
+int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream);
+
+/* Bulk-synchronous baseline on the same GPU: a gather kernel copies the
+ * shards into one contiguous M x K buffer (honouring the same schedule),
+ * then, if host_sync != 0, the host waits for the stream (the barrier), then
+ * the same GEMM kernel runs with the flags disabled. */
+int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C,
+                  const agemm_schedule* sched, int host_sync, void* stream);
+
+/* Pull model on one GPU: the GEMM reads every K-slice straight from the W
+ * shard buffers; no inbox, no flags, one kernel. */
+int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, void* stream);
+
+/* Sets the consumer's spin timeout in microseconds (default 2,000,000, or
+ * the AGEMM_SPIN_TIMEOUT_MS environment variable at create time). */
+int agemm_set_spin_timeout_us(agemm_ctx* ctx, int64_t us);
+
+/* After the caller has synchronised: AGEMM_ETIMEOUT if a consumer timed out
+ * since the last check (the error word is then cleared), else AGEMM_OK. */
+int agemm_check(agemm_ctx* ctx);
+
+/* Text of the last error on this context (never NULL). */
+const char* agemm_last_error(const agemm_ctx* ctx);
+
+/* Name of a status code (never NULL). */
+const char* agemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGEMM_H */

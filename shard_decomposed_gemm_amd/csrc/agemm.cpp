@@ -1,0 +1,458 @@
+// C-ABI of the flag-gated shard-decomposed AG+GEMM (declared in include/agemm.h).
+//
+// Host side only: validation, the context (inbox, flags, epochs, workspaces,
+// error word), stream ordering between epochs, and kernel selection. Every
+// step of the arithmetic runs in the gfx950 kernels of this directory.
+#include "agemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "agemm_internal.h"
+
+using namespace agemm;
+
+struct agemm_ctx {
+  int W = 0;
+  int64_t M = 0, K = 0, N = 0, KS = 0, bkf = 0;
+  int32_t kt = 0, t = 0;
+  agemm_dtype c_dtype = AGEMM_F16;
+  int device = 0;
+  double ticks_per_ns = 0.1;  // wall clock (kHz / 1e6)
+  uint64_t timeout_ticks = 0;
+
+  _Float16* inbox = nullptr;     // W slots of M x KS
+  uint32_t* ctrl = nullptr;      // flags[64] | t0 fused[2] (u64) | t0 bsp[2] (u64)
+  uint32_t* flags = nullptr;
+  uint64_t* t0_fused = nullptr;
+  uint64_t* t0_bsp = nullptr;
+  _Float16* gathered = nullptr;  // M x K, BSP only
+  float* ws = nullptr;           // small-M split-K workspace, T x M x N
+  uint32_t* counters = nullptr;  // small-M column-block counters
+  ErrWord* err_host = nullptr;
+  ErrWord* err_dev = nullptr;
+
+  int32_t rows_per_item = 1, items_per_tile = 1;
+  uint32_t epoch = 0;            // produce calls so far
+  uint32_t parity_fused = 0, parity_bsp = 0;
+
+  hipEvent_t ev_consumer = nullptr;  // after the last consumer call (fused, bsp or pull)
+  hipEvent_t ev_producer = nullptr;  // after the last produce call
+  bool consumer_pending = false, producer_pending = false;
+  bool consumed_this_epoch = false;
+
+  std::string last_error;
+};
+
+namespace {
+
+const char* kStatusNames[] = {"AGEMM_OK",  "AGEMM_EINVAL",   "AGEMM_ESHAPE", "AGEMM_ENOMEM",
+                              "AGEMM_EHIP", "AGEMM_ETIMEOUT", "AGEMM_ESTATE"};
+
+int fail(agemm_ctx* c, int code, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->last_error = std::string(kStatusNames[code]) + ": " + buf;
+  }
+  return code;
+}
+
+int hip_fail(agemm_ctx* c, hipError_t e, const char* what) {
+  return fail(c, AGEMM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shards(agemm_ctx* c, const void* const* a_shards) {
+  if (!a_shards) return fail(c, AGEMM_EINVAL, "a_shards is NULL");
+  for (int s = 0; s < c->W; ++s)
+    if (!aligned16(a_shards[s])) return fail(c, AGEMM_EINVAL, "a_shards[%d] is NULL or not 16-byte aligned", s);
+  return AGEMM_OK;
+}
+
+// Validates a schedule and converts it into the producer's arguments.
+int fill_schedule(agemm_ctx* c, const agemm_schedule* sched, ProduceArgs& pa) {
+  pa.has_delay = 0;
+  for (int p = 0; p < c->t; ++p) {
+    pa.order[p] = p;
+    pa.offset_ticks[p] = 0;
+  }
+  if (!sched) return AGEMM_OK;
+  if (sched->n != c->t || !sched->order || !sched->offset_ns)
+    return fail(c, AGEMM_EINVAL, "schedule must have n == T (%d) entries and non-NULL arrays", c->t);
+  bool seen[kMaxTiles] = {};
+  int64_t prev = 0;
+  for (int p = 0; p < c->t; ++p) {
+    const int32_t tile = sched->order[p];
+    if (tile < 0 || tile >= c->t || seen[tile]) return fail(c, AGEMM_EINVAL, "schedule order is not a permutation");
+    seen[tile] = true;
+    const int64_t off = sched->offset_ns[p];
+    if (off < 0 || off < prev) return fail(c, AGEMM_EINVAL, "schedule offsets must be non-negative and non-decreasing");
+    const double ticks = (double)off * c->ticks_per_ns;
+    if (ticks > 1.0e9) return fail(c, AGEMM_EINVAL, "schedule offset %lld ns is over 10 s", (long long)off);
+    prev = off;
+    pa.order[p] = tile;
+    pa.offset_ticks[p] = (uint32_t)(ticks + 0.5);
+    if (pa.offset_ticks[p]) pa.has_delay = 1;
+  }
+  return AGEMM_OK;
+}
+
+void base_produce_args(agemm_ctx* c, const void* const* a_shards, ProduceArgs& pa) {
+  for (int s = 0; s < kMaxShards; ++s)
+    pa.src[s] = s < c->W ? static_cast<const _Float16*>(a_shards[s]) : nullptr;
+  pa.M = c->M;
+  pa.KS = c->KS;
+  pa.bkf = (int32_t)c->bkf;
+  pa.kt = c->kt;
+  pa.t = c->t;
+  pa.rows_per_item = c->rows_per_item;
+  pa.items_per_tile = c->items_per_tile;
+}
+
+// Orders a new consumer after the previous one (they share the workspace and,
+// for BSP, the gathered buffer) when they are on different streams.
+int order_after_consumer(agemm_ctx* c, hipStream_t s) {
+  if (c->consumer_pending) {
+    hipError_t e = hipStreamWaitEvent(s, c->ev_consumer, 0);
+    if (e != hipSuccess) return hip_fail(c, e, "hipStreamWaitEvent");
+  }
+  return AGEMM_OK;
+}
+
+int mark_consumer(agemm_ctx* c, hipStream_t s) {
+  hipError_t e = hipEventRecord(c->ev_consumer, s);
+  if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+  c->consumer_pending = true;
+  return AGEMM_OK;
+}
+
+int ensure_small_m_workspace(agemm_ctx* c) {
+  if (c->ws) return AGEMM_OK;
+  const size_t ws_bytes = sizeof(float) * (size_t)c->t * (size_t)c->M * (size_t)c->N;
+  const size_t cnt_bytes = sizeof(uint32_t) * (size_t)small_m_column_blocks(c->N);
+  hipError_t e = hipMalloc(&c->ws, ws_bytes);
+  if (e != hipSuccess) { c->ws = nullptr; return fail(c, AGEMM_ENOMEM, "workspace of %zu bytes", ws_bytes); }
+  e = hipMalloc(&c->counters, cnt_bytes);
+  if (e != hipSuccess) { c->counters = nullptr; return fail(c, AGEMM_ENOMEM, "counters"); }
+  e = hipMemset(c->counters, 0, cnt_bytes);
+  if (e != hipSuccess) return hip_fail(c, e, "hipMemset(counters)");
+  return AGEMM_OK;
+}
+
+// Launches the GEMM (a4-a6 of the path) with the given A source and gate.
+int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* B, void* C, hipStream_t s) {
+  GemmArgs g{};
+  g.a = src;
+  g.B = static_cast<const _Float16*>(B);
+  g.C = C;
+  g.M = c->M;
+  g.N = c->N;
+  g.K = c->K;
+  g.KS = c->KS;
+  g.W = c->W;
+  g.gate = gate;
+  const bool f32 = c->c_dtype == AGEMM_F32;
+  hipError_t e;
+  if (small_m_fits(c->M, c->bkf)) {
+    int rc = ensure_small_m_workspace(c);
+    if (rc) return rc;
+    SmallMArgs sa{};
+    sa.g = g;
+    sa.ws = c->ws;
+    sa.counters = c->counters;
+    e = launch_gemm_small_m(sa, f32, s);
+  } else {
+    e = launch_gemm_mfma(g, f32, s);
+  }
+  if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
+  return AGEMM_OK;
+}
+
+Gate no_gate(agemm_ctx* c) {
+  Gate g{};
+  g.flags = nullptr;
+  g.steps_per_tile = (int32_t)(c->bkf / 64);
+  g.kt = c->kt;
+  g.t = c->t;
+  g.err = c->err_dev;
+  return g;
+}
+
+void free_all(agemm_ctx* c) {
+  if (c->inbox) hipFree(c->inbox);
+  if (c->ctrl) hipFree(c->ctrl);
+  if (c->gathered) hipFree(c->gathered);
+  if (c->ws) hipFree(c->ws);
+  if (c->counters) hipFree(c->counters);
+  if (c->err_host) hipHostFree(c->err_host);
+  if (c->ev_consumer) hipEventDestroy(c->ev_consumer);
+  if (c->ev_producer) hipEventDestroy(c->ev_producer);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* agemm_status_string(int status) {
+  if (status < 0 || status > AGEMM_ESTATE) return "AGEMM_UNKNOWN";
+  return kStatusNames[status];
+}
+
+const char* agemm_last_error(const agemm_ctx* ctx) {
+  if (!ctx) return "no context";
+  return ctx->last_error.c_str();
+}
+
+int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype, int64_t flag_ktile) {
+  if (!out) return AGEMM_EINVAL;
+  *out = nullptr;
+  if (c_dtype != AGEMM_F16 && c_dtype != AGEMM_F32) return AGEMM_EINVAL;
+  if (W < 1 || W > kMaxShards || M < 1 || M > INT32_MAX || K < 1 || N < 8) return AGEMM_ESHAPE;
+  if (K % W) return AGEMM_ESHAPE;
+  const int64_t KS = K / W;
+  if (KS % 64 || N % 8) return AGEMM_ESHAPE;
+  if (K > INT32_MAX || N > INT32_MAX) return AGEMM_ESHAPE;
+  int64_t bkf = flag_ktile;
+  if (bkf == 0) {
+    bkf = std::min<int64_t>(256, KS);
+    while ((KS / bkf) * W > kMaxTiles) {
+      int64_t next = bkf + 64;
+      while (next <= KS && KS % next) next += 64;
+      if (next > KS) return AGEMM_ESHAPE;
+      bkf = next;
+    }
+  }
+  if (bkf < 64 || bkf % 64 || KS % bkf) return AGEMM_ESHAPE;
+  if ((KS / bkf) * W > kMaxTiles) return AGEMM_ESHAPE;
+
+  agemm_ctx* c = new (std::nothrow) agemm_ctx();
+  if (!c) return AGEMM_ENOMEM;
+  c->W = W;
+  c->M = M;
+  c->K = K;
+  c->N = N;
+  c->KS = KS;
+  c->bkf = bkf;
+  c->kt = (int32_t)(KS / bkf);
+  c->t = c->kt * W;
+  c->c_dtype = c_dtype;
+  // Each producer workgroup copies about 64 KiB of one tile.
+  c->rows_per_item = (int32_t)std::max<int64_t>(1, 65536 / (bkf * 2));
+  c->items_per_tile = (int32_t)((M + c->rows_per_item - 1) / c->rows_per_item);
+
+  hipError_t e = hipGetDevice(&c->device);
+  int wall_khz = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, c->device);
+  if (e != hipSuccess || wall_khz <= 0) {
+    delete c;
+    return AGEMM_EHIP;
+  }
+  c->ticks_per_ns = (double)wall_khz / 1.0e6;
+  int64_t timeout_us = 2000000;
+  if (const char* env = std::getenv("AGEMM_SPIN_TIMEOUT_MS")) {
+    const long long ms = std::atoll(env);
+    if (ms > 0) timeout_us = ms * 1000;
+  }
+  c->timeout_ticks = (uint64_t)((double)timeout_us * 1000.0 * c->ticks_per_ns);
+
+  const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
+  const size_t ctrl_bytes = sizeof(uint32_t) * kMaxTiles + 4 * sizeof(uint64_t);
+  if (hipMalloc(&c->inbox, inbox_bytes) != hipSuccess) {
+    c->inbox = nullptr;
+    free_all(c);
+    delete c;
+    return AGEMM_ENOMEM;
+  }
+  if (hipMalloc(&c->ctrl, ctrl_bytes) != hipSuccess) {
+    c->ctrl = nullptr;
+    free_all(c);
+    delete c;
+    return AGEMM_ENOMEM;
+  }
+  c->flags = c->ctrl;
+  c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + kMaxTiles);
+  c->t0_bsp = c->t0_fused + 2;
+  void* hp = nullptr;
+  e = hipMemset(c->ctrl, 0, ctrl_bytes);
+  if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);
+  if (e == hipSuccess) {
+    c->err_host = static_cast<ErrWord*>(hp);
+    std::memset(c->err_host, 0, sizeof(ErrWord));
+    void* dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, hp, 0);
+    c->err_dev = static_cast<ErrWord*>(dp);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_consumer, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_all(c);
+    delete c;
+    return AGEMM_EHIP;
+  }
+  *out = c;
+  return AGEMM_OK;
+}
+
+int agemm_destroy(agemm_ctx* ctx) {
+  if (!ctx) return AGEMM_OK;
+  hipSetDevice(ctx->device);
+  hipDeviceSynchronize();
+  free_all(ctx);
+  delete ctx;
+  return AGEMM_OK;
+}
+
+int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (bkf) *bkf = ctx->bkf;
+  if (kt) *kt = ctx->kt;
+  if (t) *t = ctx->t;
+  return AGEMM_OK;
+}
+
+int agemm_set_spin_timeout_us(agemm_ctx* ctx, int64_t us) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (us < 1) return fail(ctx, AGEMM_EINVAL, "timeout must be positive");
+  ctx->timeout_ticks = (uint64_t)((double)us * 1000.0 * ctx->ticks_per_ns);
+  return AGEMM_OK;
+}
+
+int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_schedule* sched, void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  int rc = check_shards(ctx, a_shards);
+  if (rc) return rc;
+  ProduceArgs pa{};
+  rc = fill_schedule(ctx, sched, pa);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The inbox may be overwritten only after the consumers of the previous
+  // epoch are done with it, and producers of successive epochs run in order.
+  hipError_t e = hipSuccess;
+  if (ctx->consumer_pending) e = hipStreamWaitEvent(s, ctx->ev_consumer, 0);
+  if (e == hipSuccess && ctx->producer_pending) e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
+  base_produce_args(ctx, a_shards, pa);
+  pa.dst = ctx->inbox;
+  pa.dst_shard_stride = ctx->M * ctx->KS;
+  pa.dst_ld = ctx->KS;
+  pa.flags = ctx->flags;
+  pa.t0 = ctx->t0_fused;
+  pa.parity = ctx->parity_fused & 1u;
+  e = launch_produce(pa, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "producer launch");
+  if (pa.has_delay) ctx->parity_fused++;
+  e = hipEventRecord(ctx->ev_producer, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+  ctx->producer_pending = true;
+  ctx->epoch++;
+  ctx->consumed_this_epoch = false;
+  return AGEMM_OK;
+}
+
+int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (!aligned16(B) || !aligned16(C)) return fail(ctx, AGEMM_EINVAL, "B and C must be non-NULL and 16-byte aligned");
+  if (ctx->epoch == 0) return fail(ctx, AGEMM_ESTATE, "run_fused before any produce");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = order_after_consumer(ctx, s);
+  if (rc) return rc;
+  ASource src{};
+  for (int i = 0; i < kMaxShards; ++i) src.base[i] = i < ctx->W ? ctx->inbox + (int64_t)i * ctx->M * ctx->KS : nullptr;
+  src.lda = ctx->KS;
+  Gate gate = no_gate(ctx);
+  gate.flags = ctx->flags;
+  gate.target = ctx->epoch * (uint32_t)ctx->items_per_tile;  // wraps with the counters
+  gate.timeout_ticks = ctx->timeout_ticks;
+  rc = launch_gemm(ctx, src, gate, B, C, s);
+  if (rc) return rc;
+  ctx->consumed_this_epoch = true;
+  return mark_consumer(ctx, s);
+}
+
+int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, const agemm_schedule* sched,
+                  int host_sync, void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  int rc = check_shards(ctx, a_shards);
+  if (rc) return rc;
+  if (!aligned16(B) || !aligned16(C)) return fail(ctx, AGEMM_EINVAL, "B and C must be non-NULL and 16-byte aligned");
+  ProduceArgs pa{};
+  rc = fill_schedule(ctx, sched, pa);
+  if (rc) return rc;
+  if (!ctx->gathered) {
+    const size_t bytes = sizeof(_Float16) * (size_t)ctx->M * (size_t)ctx->K;
+    if (hipMalloc(&ctx->gathered, bytes) != hipSuccess) {
+      ctx->gathered = nullptr;
+      return fail(ctx, AGEMM_ENOMEM, "gathered A of %zu bytes", bytes);
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = order_after_consumer(ctx, s);
+  if (rc) return rc;
+  // 1) all-gather stand-in: copy the shards into one M x K buffer
+  base_produce_args(ctx, a_shards, pa);
+  pa.dst = ctx->gathered;
+  pa.dst_shard_stride = ctx->KS;
+  pa.dst_ld = ctx->K;
+  pa.flags = nullptr;
+  pa.t0 = ctx->t0_bsp;
+  pa.parity = ctx->parity_bsp & 1u;
+  hipError_t e = launch_produce(pa, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "gather launch");
+  if (pa.has_delay) ctx->parity_bsp++;
+  // 2) the bulk-synchronous barrier
+  if (host_sync) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
+  }
+  // 3) the same GEMM with the flags off, reading the gathered A
+  ASource src{};
+  for (int i = 0; i < kMaxShards; ++i) src.base[i] = i < ctx->W ? ctx->gathered + (int64_t)i * ctx->KS : nullptr;
+  src.lda = ctx->K;
+  rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
+  if (rc) return rc;
+  return mark_consumer(ctx, s);
+}
+
+int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  int rc = check_shards(ctx, a_shards);
+  if (rc) return rc;
+  if (!aligned16(B) || !aligned16(C)) return fail(ctx, AGEMM_EINVAL, "B and C must be non-NULL and 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = order_after_consumer(ctx, s);
+  if (rc) return rc;
+  ASource src{};
+  for (int i = 0; i < kMaxShards; ++i) src.base[i] = i < ctx->W ? static_cast<const _Float16*>(a_shards[i]) : nullptr;
+  src.lda = ctx->KS;
+  rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
+  if (rc) return rc;
+  return mark_consumer(ctx, s);
+}
+
+int agemm_check(agemm_ctx* ctx) {
+  if (!ctx) return AGEMM_EINVAL;
+  volatile ErrWord* w = ctx->err_host;
+  if (w->code == 0) return AGEMM_OK;
+  const unsigned tile = w->tile, target = w->target, seen = w->seen;
+  w->code = 0;
+  // A timed-out small-M launch leaves its column counters part-way; clear them.
+  if (ctx->counters) {
+    hipError_t e = hipMemset(ctx->counters, 0, sizeof(uint32_t) * (size_t)small_m_column_blocks(ctx->N));
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemset(counters)");
+  }
+  return fail(ctx, AGEMM_ETIMEOUT, "consumer gave up waiting for tile %u (flag %u, target %u)", tile, seen, target);
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal interface between the C-ABI host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace agemm {
+
+constexpr int kMaxShards = 16;
+constexpr int kMaxTiles = 64;   // T = W * KT; one wave polls every flag at once
+
+// Device error word (lives in host-pinned, device-mapped memory).
+struct ErrWord {
+  uint32_t code;     // 0 = none, 1 = flag wait timed out
+  uint32_t tile;     // tile id that timed out
+  uint32_t target;   // flag value waited for
+  uint32_t seen;     // last flag value observed
+};
+
+// Where the GEMM reads its A operand for shard s: a_base[s] + m * lda + j.
+struct ASource {
+  const _Float16* base[kMaxShards];
+  int64_t lda;
+};
+
+// Flag gate of the consumer. flags == nullptr disables gating.
+struct Gate {
+  const uint32_t* flags;
+  uint32_t target;          // epoch * contributors per tile (wrapping)
+  int32_t steps_per_tile;   // BKf / 64
+  int32_t kt;               // KT
+  int32_t t;                // T
+  uint64_t timeout_ticks;   // wall-clock ticks (100 MHz on gfx950)
+  ErrWord* err;
+};
+
+struct GemmArgs {
+  ASource a;
+  const _Float16* B;  // K x N row-major
+  void* C;            // M x N row-major, fp16 or fp32
+  int64_t M, N, K, KS;
+  int32_t W;
+  Gate gate;
+};
+
+// Producer: copies item (position p in release order, row chunk q) from A_s to
+// dst and optionally raises the tile's flag. The release schedule travels in
+// the kernel arguments (T <= 64 entries), so a call needs no allocation.
+struct ProduceArgs {
+  const _Float16* src[kMaxShards];  // A_s, M x KS
+  _Float16* dst;                    // inbox base or gathered A
+  int64_t dst_shard_stride;         // elements between shard slots (inbox: M*KS; gather: KS)
+  int64_t dst_ld;                   // row stride of dst (inbox: KS; gather: K)
+  uint32_t* flags;                  // nullptr in gather mode
+  uint64_t* t0;                     // device, 2 words: common start time per launch parity
+  uint32_t parity;
+  int32_t has_delay;                // 0: release as soon as copied
+  int64_t M, KS;
+  int32_t bkf, kt, t;
+  int32_t rows_per_item;            // rows copied by one workgroup
+  int32_t items_per_tile;           // = ceil(M / rows_per_item), contributors per flag
+  int32_t order[kMaxTiles];         // tile released p-th
+  uint32_t offset_ticks[kMaxTiles]; // its release time after the launch's start, wall-clock ticks
+};
+
+// Split-K workspace for the small-M path.
+struct SmallMArgs {
+  GemmArgs g;
+  float* ws;          // T x M x N partial sums
+  uint32_t* counters; // one per column block, zero between calls
+};
+
+hipError_t launch_produce(const ProduceArgs& a, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s);
+hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s);
+int small_m_limit();
+bool small_m_fits(int64_t M, int64_t bkf);  // small-M kernel supports this shape
+int64_t small_m_column_blocks(int64_t N);
+
+}  // namespace agemm

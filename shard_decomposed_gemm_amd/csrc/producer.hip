@@ -1,0 +1,107 @@
+// Producer of the Push model on one GPU.
+//
+// "Eliminating Multi-GPU Performance Taxes" analysis page, Push model and
+// correctness check #4: a push kernel stores each tile of shard A_s into the
+// receive buffer Inbox(s, k) and only afterwards increments the tile's ready
+// counter Flags(s, k), so that a consumer that sees the increment also sees
+// the data. Here the inbox is in local HBM; the ordering is each thread's
+// agent-scope release fence, a workgroup barrier, then one agent-scope
+// release increment per workgroup. The same kernel with flags == nullptr is
+// the gather copy of the bulk-synchronous baseline (the all-gather that
+// concatenates [A_0 | ... | A_{W-1}] along K).
+//
+// One workgroup = one work item = rows [q*R, (q+1)*R) of tile (s, kt), with
+// items ordered by release position p. A release schedule makes the item
+// wait until offset_ticks[p] after a start time shared by all workgroups of
+// the launch.
+#include "agemm_internal.h"
+
+namespace agemm {
+
+namespace {
+
+constexpr int kProducerThreads = 256;
+
+__device__ inline uint64_t wall_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+__global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a) {
+  const int item = blockIdx.x;
+  const int p = item / a.items_per_tile;
+  const int q = item - p * a.items_per_tile;
+  const int tile = a.order[p];
+  const int s = tile / a.kt;
+  const int kt = tile - s * a.kt;
+
+  if (a.has_delay) {
+    // Launches with a schedule alternate between two start-time slots; each
+    // clears the other one for the next scheduled launch (stream-ordered).
+    if (threadIdx.x == 0) {
+      const uint64_t now = wall_clock();
+      unsigned long long expected = 0;
+      // The first workgroup to arrive fixes the launch's start time.
+      __hip_atomic_compare_exchange_strong(reinterpret_cast<unsigned long long*>(a.t0 + a.parity), &expected,
+                                           (unsigned long long)now, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t base = expected ? (uint64_t)expected : now;
+      const uint64_t due = base + (uint64_t)a.offset_ticks[p];
+      while (wall_clock() < due) __builtin_amdgcn_s_sleep(8);
+      if (item == 0)
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.t0 + (a.parity ^ 1u)), 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+
+  const int64_t r0 = (int64_t)q * a.rows_per_item;
+  int64_t r1 = r0 + a.rows_per_item;
+  if (r1 > a.M) r1 = a.M;
+  const int cpr = a.bkf >> 3;  // 16-byte chunks per row segment
+  const int64_t total = (r1 - r0) * cpr;
+  const _Float16* __restrict__ src = a.src[s] + (int64_t)kt * a.bkf;
+  _Float16* __restrict__ dst = a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * a.bkf;
+
+  constexpr int U = 4;
+  int64_t c = threadIdx.x;
+  for (; c + (U - 1) * kProducerThreads < total; c += U * kProducerThreads) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cc = c + u * kProducerThreads;
+      const int64_t row = r0 + cc / cpr;
+      const int col = (int)(cc % cpr);
+      v[u] = *reinterpret_cast<const uint4*>(src + row * a.KS + col * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cc = c + u * kProducerThreads;
+      const int64_t row = r0 + cc / cpr;
+      const int col = (int)(cc % cpr);
+      *reinterpret_cast<uint4*>(dst + row * a.dst_ld + col * 8) = v[u];
+    }
+  }
+  for (; c < total; c += kProducerThreads) {
+    const int64_t row = r0 + c / cpr;
+    const int col = (int)(c % cpr);
+    *reinterpret_cast<uint4*>(dst + row * a.dst_ld + col * 8) =
+        *reinterpret_cast<const uint4*>(src + row * a.KS + col * 8);
+  }
+
+  if (a.flags) {
+    // Make this thread's stores visible at agent scope, gather the workgroup,
+    // then publish the tile with one release increment.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(a.flags + tile, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_produce(const ProduceArgs& a, hipStream_t s) {
+  const unsigned items = (unsigned)a.t * (unsigned)a.items_per_tile;
+  hipLaunchKernelGGL(produce_kernel, dim3(items), dim3(kProducerThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace agemm

@@ -1,0 +1,71 @@
+"""The C-ABI library loads, exports every function include/agemm.h declares,
+and rejects bad shapes before touching the GPU. No compute calls here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from shard_decomposed_gemm_amd import agemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "agemm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(agemm_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = _declared()
+    for must in ("agemm_create", "agemm_produce", "agemm_run_fused", "agemm_run_bsp"):
+        assert must in names
+    assert sorted(agemm.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = agemm.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert agemm.status_string(0) == "AGEMM_OK"
+    assert agemm.status_string(5) == "AGEMM_ETIMEOUT"
+    assert agemm.status_string(99) == "AGEMM_UNKNOWN"
+
+
+@pytest.mark.parametrize("W,M,K,N,code", [
+    (0, 1, 512, 256, agemm.ESHAPE),     # no shards
+    (17, 1, 17 * 64, 256, agemm.ESHAPE),  # too many shards
+    (8, 0, 512, 256, agemm.ESHAPE),     # empty M
+    (8, 1, 500, 256, agemm.ESHAPE),     # K not a multiple of W
+    (8, 1, 8 * 96, 256, agemm.ESHAPE),  # K/W not a multiple of 64
+    (8, 1, 512, 250, agemm.ESHAPE),     # N not a multiple of 8
+    (8, 1, 512, 0, agemm.ESHAPE),
+])
+def test_create_rejects_bad_shapes_without_gpu(W, M, K, N, code):
+    lib = agemm.load()
+    h = ctypes.c_void_p()
+    assert lib.agemm_create(ctypes.byref(h), W, M, K, N, agemm.F16, 0) == code
+    assert not h.value
+
+
+def test_create_rejects_bad_flag_tile_and_dtype():
+    lib = agemm.load()
+    h = ctypes.c_void_p()
+    assert lib.agemm_create(ctypes.byref(h), 8, 4, 8192, 256, agemm.F16, 96) == agemm.ESHAPE   # not /64
+    assert lib.agemm_create(ctypes.byref(h), 8, 4, 8192, 256, agemm.F16, 384) == agemm.ESHAPE  # does not divide 1024
+    assert lib.agemm_create(ctypes.byref(h), 16, 4, 16 * 4096, 256, agemm.F16, 64) == agemm.ESHAPE  # T > 64
+    assert lib.agemm_create(ctypes.byref(h), 8, 4, 8192, 256, 7, 0) == agemm.EINVAL
+    assert lib.agemm_create(None, 8, 4, 8192, 256, agemm.F16, 0) == agemm.EINVAL
+
+
+def test_null_context_is_rejected():
+    lib = agemm.load()
+    assert lib.agemm_run_fused(None, None, None, None) == agemm.EINVAL
+    assert lib.agemm_produce(None, None, None, None) == agemm.EINVAL
+    assert lib.agemm_check(None) == agemm.EINVAL
+    assert lib.agemm_destroy(None) == agemm.OK
+    assert lib.agemm_last_error(None) == b"no context"

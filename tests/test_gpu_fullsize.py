@@ -1,0 +1,68 @@
+"""Full-size workloads (K = 8192, N = 28672, W = 8) in the launch configuration the
+benchmark times: sampled entries against the oracle, and every entry compared
+across the fused, bulk-synchronous and pull paths (same kernels, same summation
+order, so the three must agree bit for bit).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+W, K, N = 8, 8192, 28672
+CONFIGS = {
+    # name: (M, schedule?)
+    "decode_m1": (1, False),
+    "xover_m128": (128, False),
+    "prefill_m4096": (4096, False),
+    "ooo_m512": (512, True),
+}
+
+
+@pytest.fixture(scope="module")
+def weight():
+    b = synth.matrix_f16(0xB002, K, N)
+    return b, gu.to_dev(b)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_full_size(name, weight):
+    import torch
+    from shard_decomposed_gemm_amd import Context
+    M, scheduled = CONFIGS[name]
+    b, B = weight
+    a = synth.matrix_f16(0xA100 + M, M, K)
+    sh = synth.shards(a, W)
+    dsh = [gu.to_dev(s) for s in sh]
+    ctx = Context(W, M, K, N, c_dtype="f16")
+    sched = synth.schedule(0x5005, ctx.t, 20_000) if scheduled else None
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    Cf = gu.empty_c(M, N, "f16")
+    ctx.produce(dsh, schedule=sched, stream=sp)
+    ctx.run_fused(B, Cf, stream=sc)
+    torch.cuda.synchronize()
+    ctx.check()
+    Cb = gu.empty_c(M, N, "f16")
+    ctx.run_bsp(dsh, B, Cb, schedule=sched, host_sync=True)
+    Cp = gu.empty_c(M, N, "f16")
+    ctx.run_pull(dsh, B, Cp)
+    torch.cuda.synchronize()
+    ctx.check()
+    assert torch.equal(Cf.view(torch.int16), Cb.view(torch.int16))
+    assert torch.equal(Cf.view(torch.int16), Cp.view(torch.int16))
+    got = Cf.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(M)
+    n_samp = 4096
+    rows = rng.integers(0, M, n_samp)
+    cols = rng.integers(0, N, n_samp)
+    # always include the corners and the shard-tile boundaries of the grid
+    rows[:4] = [0, M - 1, 0, M - 1]
+    cols[:4] = [0, 0, N - 1, N - 1]
+    ref = oracle.sharded_gemm_entries(sh, b, rows, cols)
+    err = np.abs(got[rows, cols] - ref).max()
+    assert err <= oracle.tolerance(K), err
+    ctx.close()

@@ -1,0 +1,130 @@
+"""Flag gating on the GPU: the consumer never reads a k-tile before its flag.
+
+Source of the invariant: "Eliminating Multi-GPU Performance Taxes" analysis
+page, correctness check #4 (the store precedes the flag increment, so a
+consumer that sees the flag sees the data).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _ctx(W, M, K, N, c_dtype="f16"):
+    from shard_decomposed_gemm_amd import Context
+    return Context(W, M, K, N, c_dtype=c_dtype)
+
+
+@pytest.mark.parametrize("W,M,K,N", [(8, 1, 2048, 1024), (8, 4, 4096, 2056), (8, 96, 2048, 1024), (8, 512, 2048, 1024)])
+def test_poisoned_inbox_is_never_read_early(W, M, K, N):
+    """Epoch 1 fills the inbox with NaN; epoch 2 releases real tiles late and out of
+    order while the consumer is already running. Any premature read would show NaN."""
+    import torch
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=41)
+    ref = oracle.sharded_gemm(sh, b)
+    ctx = _ctx(W, M, K, N, "f32")
+    nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
+    ctx.produce(nan)
+    torch.cuda.synchronize()
+    order, offs = synth.schedule(0x5100 + M, ctx.t, 40_000)  # up to 40 us between releases
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    C = gu.empty_c(M, N, "f32")
+    ctx.produce(dsh, schedule=(order, offs), stream=sp)
+    ctx.run_fused(B, C, stream=sc)
+    torch.cuda.synchronize()
+    ctx.check()
+    got = gu.c_to_f64(C)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= oracle.tolerance(K)
+
+
+@pytest.mark.parametrize("M", [1, 256])
+def test_alternating_epochs(M):
+    """Two data sets alternate over successive epochs on two streams; each epoch's C
+    must match its own data (the inbox is not overwritten while still being read)."""
+    import torch
+    W, K, N = 8, 2048, 1024
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (51, 52)]
+    refs = [oracle.sharded_gemm(p[1], p[2]) for p in probs]
+    ctx = _ctx(W, M, K, N, "f32")
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for e in range(6):
+        p = probs[e % 2]
+        C = gu.empty_c(M, N, "f32")
+        order, offs = synth.schedule(0x5200 + e, ctx.t, 5_000 if e % 3 == 0 else 0)
+        ctx.produce(p[3], schedule=(order, offs), stream=sp)
+        ctx.run_fused(p[4], C, stream=sc)
+        outs.append(C)
+    torch.cuda.synchronize()
+    ctx.check()
+    for e, C in enumerate(outs):
+        assert np.abs(gu.c_to_f64(C) - refs[e % 2]).max() <= oracle.tolerance(K), e
+
+
+@pytest.mark.parametrize("M", [2, 300])
+def test_timeout_reports_and_recovers(M):
+    """A tile released long after the consumer's spin timeout: the consumer stops,
+    agemm_check reports ETIMEOUT, and the next epoch is correct again."""
+    import torch
+    from shard_decomposed_gemm_amd import AgemmError
+    from shard_decomposed_gemm_amd.agemm import ETIMEOUT
+    W, K, N = 8, 2048, 1024
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=61)
+    ref = oracle.sharded_gemm(sh, b)
+    ctx = _ctx(W, M, K, N, "f32")
+    ctx.set_spin_timeout_us(2_000)
+    order = np.arange(ctx.t, dtype=np.int32)
+    offs = np.zeros(ctx.t, dtype=np.int64)
+    offs[-1] = 30_000_000  # last tile 30 ms late
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    C = gu.empty_c(M, N, "f32")
+    ctx.produce(dsh, schedule=(order, offs), stream=sp)
+    ctx.run_fused(B, C, stream=sc)
+    torch.cuda.synchronize()
+    with pytest.raises(AgemmError) as ei:
+        ctx.check()
+    assert ei.value.status == ETIMEOUT
+    ctx.check()  # the error word is cleared
+    ctx.set_spin_timeout_us(2_000_000)
+    C2 = gu.empty_c(M, N, "f32")
+    ctx.produce(dsh, stream=sp)
+    ctx.run_fused(B, C2, stream=sc)
+    torch.cuda.synchronize()
+    ctx.check()
+    assert np.abs(gu.c_to_f64(C2) - ref).max() <= oracle.tolerance(K)
+
+
+def test_call_order_and_argument_errors():
+    import torch
+    from shard_decomposed_gemm_amd import AgemmError
+    from shard_decomposed_gemm_amd.agemm import EINVAL, ESTATE
+    W, M, K, N = 8, 16, 1024, 256
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=71)
+    ctx = _ctx(W, M, K, N, "f16")
+    C = gu.empty_c(M, N, "f16")
+    with pytest.raises(AgemmError) as ei:
+        ctx.run_fused(B, C)
+    assert ei.value.status == ESTATE
+    bad = (np.arange(ctx.t)[::-1].copy(), np.array([5] + [0] * (ctx.t - 1)))  # offsets decrease
+    with pytest.raises(AgemmError) as ei:
+        ctx.produce(dsh, schedule=bad)
+    assert ei.value.status == EINVAL
+    dup = (np.zeros(ctx.t, dtype=np.int32), np.zeros(ctx.t, dtype=np.int64))  # not a permutation
+    with pytest.raises(AgemmError) as ei:
+        ctx.produce(dsh, schedule=dup)
+    assert ei.value.status == EINVAL
+    # a misaligned C (2-byte offset) is rejected before any launch
+    big = torch.empty(M * N + 1, dtype=torch.float16, device=gu.dev())
+    ctx.produce(dsh)
+    with pytest.raises(AgemmError) as ei:
+        import ctypes
+        from shard_decomposed_gemm_amd import agemm
+        rc = agemm.load().agemm_run_fused(ctx._h, B.data_ptr(), big.data_ptr() + 2, None)
+        ctx._raise(rc, "agemm_run_fused")
+    assert ei.value.status == EINVAL
+    torch.cuda.synchronize()
