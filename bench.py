@@ -1,0 +1,214 @@
+"""Benchmark of the flag-gated shard-decomposed AG+GEMM on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the producer fills
+the inbox and raises the per-(shard, k-tile) flags on one stream while the
+flag-gated consumer GEMM runs on another (the Push model of the "Eliminating
+Multi-GPU Performance Taxes" analysis page). Inputs are seeded synthetic fp16
+uniform[-1, 1] and resident in HBM before timing starts.
+
+Prints one JSON line. Besides the required fields it carries:
+  roofline      the consumer kernel (the dominant one) against the fp16 MFMA
+                or HBM peak, timed with HIP events on the consumer's stream;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
+  ladder        the same-GPU BSP ladder: BSP with host barrier, BSP with a
+                device-side dependency only, fused, consumer alone (flags set).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+W_DEF, K_DEF, N_DEF = 8, 8192, 28672
+WORKLOADS = {
+    # name: (W, M, K, N, c_dtype, release schedule)
+    "tiny_m8": (8, 8, 512, 256, "f32", None),
+    "decode_m1": (W_DEF, 1, K_DEF, N_DEF, "f16", None),
+    "xover_m128": (W_DEF, 128, K_DEF, N_DEF, "f16", None),
+    "prefill_m4096": (W_DEF, 4096, K_DEF, N_DEF, "f16", None),
+    "ooo_m512": (W_DEF, 512, K_DEF, N_DEF, "f16", "random"),
+}
+# MI355X published peaks
+PEAK_FP16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic(W, M, K, N, c_bytes):
+    flops = 2.0 * M * K * N
+    consumer_bytes = 2.0 * K * N + 2.0 * M * K + c_bytes * M * N  # B once, A once, C once
+    path_bytes = 2.0 * K * N + 6.0 * M * K + c_bytes * M * N      # + producer read and inbox write
+    return flops, consumer_bytes, path_bytes
+
+
+def cpu_baseline(W, M, K, N, budget_s: float):
+    """The oracle as it stands, on a bounded row sample of the same workload."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = oracle.default_threads()
+    b = synth.matrix_f16(0xB002, K, N)
+    # rows per second of the oracle: measure one row first, then size the sample
+    rows = 1
+    a = synth.matrix_f16(0xA102, max(M, 1), K)
+    t0 = time.perf_counter()
+    oracle.sharded_gemm(synth.shards(a[:rows], W), b, nthreads=threads)
+    t1 = time.perf_counter() - t0
+    rows = int(max(1, min(M, threads * max(1, int(budget_s / max(t1, 1e-6) / threads)))))
+    rows = min(rows, M)
+    if rows > 1:
+        t0 = time.perf_counter()
+        oracle.sharded_gemm(synth.shards(a[:rows], W), b, nthreads=threads)
+        t1 = time.perf_counter() - t0
+    flops = 2.0 * rows * K * N
+    return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": min(threads, rows),
+            "kind": "oracle", "sample": f"{rows} of {M} rows at full K={K}, N={N}, W={W} (binary64, {t1:.2f} s)",
+            "seconds": t1}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_m1", choices=list(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ladder", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the flag-gated path keeps all W inbox slots in one GPU's HBM "
+              "and this build has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from shard_decomposed_gemm_amd import Context
+
+    W, M, K, N, c_dtype, sched_kind = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={args.workload} W={W} M={M} K={K} N={N} C={c_dtype}", file=sys.stderr, flush=True)
+
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).to(dev)
+    a = synth.matrix_f16(0xA102, M, K)
+    shards = [to_dev(s) for s in synth.shards(a, W)]
+    B0 = to_dev(synth.matrix_f16(0xB002, K, N))
+    # Two copies of B, used alternately, so that the 256 MB last-level cache cannot hold B across steps.
+    Bs = [B0, B0.clone()]
+    cdt = torch.float16 if c_dtype == "f16" else torch.float32
+    c_bytes = 2 if c_dtype == "f16" else 4
+    Cs = [torch.empty((M, N), dtype=cdt, device=dev) for _ in range(2)]
+    ctx = Context(W, M, K, N, c_dtype=c_dtype)
+    sched = synth.schedule(0x5005, ctx.t, 20_000) if sched_kind == "random" else None
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def fused_step(i):
+        ctx.produce(shards, schedule=sched, stream=sp)
+        ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc)
+
+    # ---- the timed fused steps, with per-launch HIP events on the consumer stream
+    for i in range(args.warmup):
+        fused_step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ctx.produce(shards, schedule=sched, stream=sp)
+        ev[i][0].record(sc)
+        ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc)
+        ev[i][1].record(sc)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ctx.check()
+    kern_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_step = wall * 1e3 / args.steps
+    flops, cons_bytes, path_bytes = algorithmic(W, M, K, N, c_bytes)
+    value = flops / (ms_step * 1e-3) / 1e12
+    kavg = float(np.mean(kern_ms))
+    print(f"[bench] fused: {ms_step * 1e3:.1f} us/step, consumer kernel {kavg * 1e3:.1f} us avg", file=sys.stderr,
+          flush=True)
+
+    mfma_bound = flops / (PEAK_FP16_TFLOPS * 1e12) > cons_bytes / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved = flops / (kavg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None}
+    else:
+        achieved = cons_bytes / (kavg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    roof["kernel"] = "consumer GEMM (flag-gated)"
+    roof["algorithmic_bytes_per_launch"] = cons_bytes
+    roof["flops_per_launch"] = flops
+    roof["kernel_us_avg"] = kavg * 1e3
+
+    # ---- the BSP ladder on the same GPU
+    ladder = None
+    if not args.no_ladder:
+        def timeit(fn, n):
+            for i in range(max(3, n // 5)):
+                fn(i)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(n):
+                fn(i)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) * 1e6 / n
+
+        n = args.steps
+        bsp_sync = timeit(lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched, host_sync=True,
+                                                stream=sc), n)
+        bsp_dev = timeit(lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched, host_sync=False,
+                                               stream=sc), n)
+        fused = timeit(fused_step, n)
+        ctx.produce(shards)
+        torch.cuda.synchronize()
+        consumer_only = timeit(lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), n)
+        pull = timeit(lambda i: ctx.run_pull(shards, Bs[i & 1], Cs[i & 1], stream=sc), n)
+        ctx.check()
+        ladder = {"bsp_host_sync_us": bsp_sync, "bsp_device_dep_us": bsp_dev, "fused_us": fused,
+                  "consumer_only_us": consumer_only, "pull_us": pull,
+                  "fused_speedup_vs_bsp": bsp_sync / fused}
+        print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(W, M, K, N, args.cpu_budget)
+        print(f"[bench] cpu oracle: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "TFLOP/s and % fp16 MFMA / HBM roofline, shard-split GEMM K=8192 N=28672",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "W": W, "M": M, "K": K, "N": N, "c_dtype": c_dtype,
+                   "accumulate": "f32", "flag_ktile": ctx.bkf, "tiles": ctx.t,
+                   "schedule": "seeded permutation, cumulative U[0,20] us delays" if sched else "shard order, no delay",
+                   "path": "producer || flag-gated consumer on two streams"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "ladder": ladder,
+    }
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,7 @@ struct agemm_ctx {
   int32_t kt = 0, t = 0;
   agemm_dtype c_dtype = AGEMM_F16;
   int device = 0;
+  int num_cus = 0;
   double ticks_per_ns = 0.1;  // wall clock (kHz / 1e6)
   uint64_t timeout_ticks = 0;
 
@@ -137,19 +138,6 @@ int mark_consumer(agemm_ctx* c, hipStream_t s) {
   return AGEMM_OK;
 }
 
-int ensure_small_m_workspace(agemm_ctx* c) {
-  if (c->ws) return AGEMM_OK;
-  const size_t ws_bytes = sizeof(float) * (size_t)c->t * (size_t)c->M * (size_t)c->N;
-  const size_t cnt_bytes = sizeof(uint32_t) * (size_t)small_m_column_blocks(c->N);
-  hipError_t e = hipMalloc(&c->ws, ws_bytes);
-  if (e != hipSuccess) { c->ws = nullptr; return fail(c, AGEMM_ENOMEM, "workspace of %zu bytes", ws_bytes); }
-  e = hipMalloc(&c->counters, cnt_bytes);
-  if (e != hipSuccess) { c->counters = nullptr; return fail(c, AGEMM_ENOMEM, "counters"); }
-  e = hipMemset(c->counters, 0, cnt_bytes);
-  if (e != hipSuccess) return hip_fail(c, e, "hipMemset(counters)");
-  return AGEMM_OK;
-}
-
 // Launches the GEMM (a4-a6 of the path) with the given A source and gate.
 int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* B, void* C, hipStream_t s) {
   GemmArgs g{};
@@ -161,12 +149,11 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.K = c->K;
   g.KS = c->KS;
   g.W = c->W;
+  g.num_cus = c->num_cus;
   g.gate = gate;
   const bool f32 = c->c_dtype == AGEMM_F32;
   hipError_t e;
-  if (small_m_fits(c->M, c->bkf)) {
-    int rc = ensure_small_m_workspace(c);
-    if (rc) return rc;
+  if (c->ws) {
     SmallMArgs sa{};
     sa.g = g;
     sa.ws = c->ws;
@@ -254,7 +241,8 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   hipError_t e = hipGetDevice(&c->device);
   int wall_khz = 0;
   if (e == hipSuccess) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, c->device);
-  if (e != hipSuccess || wall_khz <= 0) {
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e != hipSuccess || wall_khz <= 0 || c->num_cus <= 0) {
     delete c;
     return AGEMM_EHIP;
   }
@@ -266,16 +254,23 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   }
   c->timeout_ticks = (uint64_t)((double)timeout_us * 1000.0 * c->ticks_per_ns);
 
+  // Everything the context owns is allocated (and zeroed) here, so no call
+  // on the hot path allocates or relies on an unordered memset.
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
+  const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
   const size_t ctrl_bytes = sizeof(uint32_t) * kMaxTiles + 4 * sizeof(uint64_t);
-  if (hipMalloc(&c->inbox, inbox_bytes) != hipSuccess) {
-    c->inbox = nullptr;
-    free_all(c);
-    delete c;
-    return AGEMM_ENOMEM;
+  const bool small = small_m_fits(M, bkf);
+  const size_t ws_bytes = small ? sizeof(float) * (size_t)c->t * (size_t)M * (size_t)N : 0;
+  const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)small_m_column_blocks(N) : 0;
+  bool ok = hipMalloc(&c->inbox, inbox_bytes) == hipSuccess;
+  ok = ok && hipMalloc(&c->gathered, gathered_bytes) == hipSuccess;
+  ok = ok && hipMalloc(&c->ctrl, ctrl_bytes) == hipSuccess;
+  if (ok && small) {
+    ok = hipMalloc(&c->ws, ws_bytes) == hipSuccess;
+    ok = ok && hipMalloc(&c->counters, cnt_bytes) == hipSuccess;
+    ok = ok && hipMemset(c->counters, 0, cnt_bytes) == hipSuccess;
   }
-  if (hipMalloc(&c->ctrl, ctrl_bytes) != hipSuccess) {
-    c->ctrl = nullptr;
+  if (!ok) {
     free_all(c);
     delete c;
     return AGEMM_ENOMEM;
@@ -390,13 +385,6 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   ProduceArgs pa{};
   rc = fill_schedule(ctx, sched, pa);
   if (rc) return rc;
-  if (!ctx->gathered) {
-    const size_t bytes = sizeof(_Float16) * (size_t)ctx->M * (size_t)ctx->K;
-    if (hipMalloc(&ctx->gathered, bytes) != hipSuccess) {
-      ctx->gathered = nullptr;
-      return fail(ctx, AGEMM_ENOMEM, "gathered A of %zu bytes", bytes);
-    }
-  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = order_after_consumer(ctx, s);
   if (rc) return rc;
@@ -450,6 +438,7 @@ int agemm_check(agemm_ctx* ctx) {
   // A timed-out small-M launch leaves its column counters part-way; clear them.
   if (ctx->counters) {
     hipError_t e = hipMemset(ctx->counters, 0, sizeof(uint32_t) * (size_t)small_m_column_blocks(ctx->N));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemset(counters)");
   }
   return fail(ctx, AGEMM_ETIMEOUT, "consumer gave up waiting for tile %u (flag %u, target %u)", tile, seen, target);

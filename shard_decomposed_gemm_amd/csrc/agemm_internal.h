@@ -40,6 +40,7 @@ struct GemmArgs {
   void* C;            // M x N row-major, fp16 or fp32
   int64_t M, N, K, KS;
   int32_t W;
+  int32_t num_cus;    // compute units of the device (persistent grid size)
   Gate gate;
 };
 

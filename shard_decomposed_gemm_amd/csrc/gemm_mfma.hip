@@ -131,52 +131,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   const int64_t M = g.M, N = g.N;
   const int MB = (int)((M + BM - 1) / BM);
   const int NB = (int)((N + BN - 1) / BN);
-
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of logical tiles, ordered in groups of 8 row-blocks so
-  // that concurrently running tiles on one XCD share A and B rows in its L2.
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
-  const int logical = (G % 8 == 0) ? (b % 8) * (G / 8) + (b / 8) : b;
-  constexpr int GM = 8;
-  const int group = logical / (GM * NB);
-  const int first_m = group * GM;
-  const int gsize = (MB - first_m) < GM ? (MB - first_m) : GM;
-  const int in_group = logical - group * GM * NB;
-  const int mb = first_m + in_group % gsize;
-  const int nb = in_group / gsize;
-  const int64_t m0 = (int64_t)mb * BM;
-  const int64_t n0 = (int64_t)nb * BN;
-
+  const int total = MB * NB;
   const int SPS = (int)(g.KS / BK);  // k-steps per shard
   const int NS = (int)(g.K / BK);    // k-steps in all
 
-  // Global source offsets (elements) of this thread's 16-byte chunks; the
-  // LDS destination of chunk q is byte q*16 of the stage.
-  int64_t a_off[A_ITERS];
-#pragma unroll
-  for (int j = 0; j < A_ITERS; ++j) {
-    const int q = j * NT + wave * 64 + lane;
-    const int r = q >> 3;
-    const int c = (q & 7) ^ (r & 7);
-    int64_t m = m0 + r;
-    if (m > M - 1) m = M - 1;  // rows past M load a valid row; their results are not stored
-    a_off[j] = m * g.a.lda + c * 8;
-  }
-  int64_t b_off[B_ITERS];
-#pragma unroll
-  for (int j = 0; j < B_ITERS; ++j) {
-    const int q = j * NT + wave * 64 + lane;
-    const int k = q / CPR_B;
-    const int c = (q % CPR_B) ^ swz_b(k);
-    int64_t n = n0 + c * 8;
-    if (n > N - 8) n = N - 8;
-    b_off[j] = (int64_t)k * N + n;
-  }
-
-  // LDS read offsets. A: row (wm*TM + fm*32 + lane%32), 16-byte chunk
-  // (2*ks + lane/32) ^ (row & 7). B (transpose read, 16-lane groups): lane
-  // supplies row k = 16*ks + 8*(g/2) + 4*h + (i/4) and columns
+  // LDS read offsets (tile independent). A: row (wm*TM + fm*32 + lane%32),
+  // 16-byte chunk (2*ks + lane/32) ^ (row & 7). B (transpose read, 16-lane
+  // groups): lane supplies row k = 16*ks + 8*(g/2) + 4*h + (i/4) and columns
   // n = fn*32 + 16*(g%2) + 4*(i%4) of the wave's range, chunk (n/8) ^ swz(k);
   // swz(k) does not depend on ks or h.
   ReadOffsets ro;
@@ -193,7 +154,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     }
   }
 
-  uint64_t ready = 0;
+  uint64_t ready = 0;  // flags this workgroup has already acquired (persists across its tiles)
   // Returns false if the workgroup must stop (flag wait timed out).
   auto gate = [&](int t) -> bool {
     if constexpr (!GATED) {
@@ -243,73 +204,117 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // Persistent loop over output tiles. Workgroups are dealt round-robin to
+  // the 8 XCDs; each XCD gets a contiguous range of logical tiles, ordered in
+  // groups of 8 row-blocks, so tiles running together on one XCD share A and
+  // B rows in its L2.
+  const int G = gridDim.x;
+  const bool xcd_split = (total % 8 == 0) && (G % 8 == 0);
+  bool ok = true;
+  for (int w = blockIdx.x; w < total; w += G) {
+    const int logical = xcd_split ? (w % 8) * (total / 8) + (w / 8) : w;
+    constexpr int GM = 8;
+    const int group = logical / (GM * NB);
+    const int first_m = group * GM;
+    const int gsize = (MB - first_m) < GM ? (MB - first_m) : GM;
+    const int in_group = logical - group * GM * NB;
+    const int mb = first_m + in_group % gsize;
+    const int nb = in_group / gsize;
+    const int64_t m0 = (int64_t)mb * BM;
+    const int64_t n0 = (int64_t)nb * BN;
 
-  auto a_src = [&](int t) {
-    const int s = t / SPS;
-    return g.a.base[s] + (int64_t)(t - s * SPS) * BK;
-  };
-  auto b_src = [&](int t) { return g.B + (int64_t)t * BK * N; };
+    // Global source offsets (elements) of this thread's 16-byte chunks; the
+    // LDS destination of chunk q is byte q*16 of the stage.
+    int64_t a_off[A_ITERS];
+#pragma unroll
+    for (int j = 0; j < A_ITERS; ++j) {
+      const int q = j * NT + wave * 64 + lane;
+      const int r = q >> 3;
+      const int c = (q & 7) ^ (r & 7);
+      int64_t m = m0 + r;
+      if (m > M - 1) m = M - 1;  // rows past M load a valid row; their results are not stored
+      a_off[j] = m * g.a.lda + c * 8;
+    }
+    int64_t b_off[B_ITERS];
+#pragma unroll
+    for (int j = 0; j < B_ITERS; ++j) {
+      const int q = j * NT + wave * 64 + lane;
+      const int k = q / CPR_B;
+      const int c = (q % CPR_B) ^ swz_b(k);
+      int64_t n = n0 + c * 8;
+      if (n > N - 8) n = N - 8;
+      b_off[j] = (int64_t)k * N + n;
+    }
 
-  bool ok = gate(0);
-  if (ok) {
-    const _Float16* as = a_src(0);
-    const _Float16* bs = b_src(0);
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int j = 0; j < A_ITERS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(as + a_off[j]), (LDS_PTR(void))(smem + (j * NT + wave * 64) * 16),
-                                       16, 0, 0);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < B_ITERS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(bs + b_off[j]),
-                                       (LDS_PTR(void))(smem + A_BYTES + (j * NT + wave * 64) * 16), 16, 0, 0);
-  }
-  // One loop body for every k-step (a single copy of the MFMA code keeps the
-  // accumulators in place). The last step re-issues its own loads into the
-  // idle stage, which nobody reads; they are drained before the epilogue.
-  for (int t = 0; ok && t < NS; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int tn = (t + 1 < NS) ? t + 1 : t;
-    ok = gate(tn);
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto a_src = [&](int t) {
+      const int s = t / SPS;
+      return g.a.base[s] + (int64_t)(t - s * SPS) * BK;
+    };
+    auto b_src = [&](int t) { return g.B + (int64_t)t * BK * N; };
+
+    __syncthreads();  // the previous tile's last reads of LDS are done
+    ok = gate(0);
     if (!ok) break;
-    kstep<BM, BN, WM, WN, true>(smem + ((t + 1) & 1) * STAGE, smem + (t & 1) * STAGE, a_src(tn), b_src(tn), a_off,
-                                b_off, wave, ro, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the direct loads before leaving or storing
-  if (!ok) return;                 // a flag wait timed out: C is left undefined
+    {
+      const _Float16* as = a_src(0);
+      const _Float16* bs = b_src(0);
+#pragma unroll
+      for (int j = 0; j < A_ITERS; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(as + a_off[j]),
+                                         (LDS_PTR(void))(smem + (j * NT + wave * 64) * 16), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < B_ITERS; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(bs + b_off[j]),
+                                         (LDS_PTR(void))(smem + A_BYTES + (j * NT + wave * 64) * 16), 16, 0, 0);
+    }
+    // One loop body for every k-step (a single copy of the MFMA code keeps the
+    // accumulators in place). The last step re-issues its own loads into the
+    // idle stage, which nobody reads; they are drained before the epilogue.
+    for (int t = 0; t < NS; ++t) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const int tn = (t + 1 < NS) ? t + 1 : t;
+      ok = gate(tn);
+      if (!ok) break;
+      kstep<BM, BN, WM, WN, true>(smem + ((t + 1) & 1) * STAGE, smem + (t & 1) * STAGE, a_src(tn), b_src(tn), a_off,
+                                  b_off, wave, ro, acc);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // drain the direct loads before storing or leaving
+    if (!ok) break;                  // a flag wait timed out: C is left undefined
 
-  // Epilogue: lane holds C[m][n .. n+3] for m = lane % 32 of each 32-row block.
+    // Epilogue: lane holds C[m][n .. n+3] for m = lane % 32 of each 32-row block.
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int64_t m = m0 + wm * TM + fm * 32 + (lane & 31);
-    if (m >= M) continue;
+    for (int fm = 0; fm < FM; ++fm) {
+      const int64_t m = m0 + wm * TM + fm * 32 + (lane & 31);
+      if (m >= M) continue;
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      // Keep the accumulator reads of one 32x32 block together so the
-      // epilogue does not pull all 256 accumulators into VGPRs at once.
-      __builtin_amdgcn_sched_barrier(0);
+      for (int fn = 0; fn < FN; ++fn) {
+        // Keep the accumulator reads of one 32x32 block together.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * TN + fn * 32 + q * 8 + (lane >> 5) * 4;
-        if (n >= N) continue;
-        if constexpr (OUTF32) {
-          float4 v = make_float4(acc[fm][fn][q * 4 + 0], acc[fm][fn][q * 4 + 1], acc[fm][fn][q * 4 + 2],
-                                 acc[fm][fn][q * 4 + 3]);
-          *reinterpret_cast<float4*>(static_cast<float*>(g.C) + m * N + n) = v;
-        } else {
-          half4 v;
-          v[0] = (_Float16)acc[fm][fn][q * 4 + 0];
-          v[1] = (_Float16)acc[fm][fn][q * 4 + 1];
-          v[2] = (_Float16)acc[fm][fn][q * 4 + 2];
-          v[3] = (_Float16)acc[fm][fn][q * 4 + 3];
-          *reinterpret_cast<half4*>(static_cast<_Float16*>(g.C) + m * N + n) = v;
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = n0 + wn * TN + fn * 32 + q * 8 + (lane >> 5) * 4;
+          if (n >= N) continue;
+          if constexpr (OUTF32) {
+            float4 v = make_float4(acc[fm][fn][q * 4 + 0], acc[fm][fn][q * 4 + 1], acc[fm][fn][q * 4 + 2],
+                                   acc[fm][fn][q * 4 + 3]);
+            *reinterpret_cast<float4*>(static_cast<float*>(g.C) + m * N + n) = v;
+          } else {
+            half4 v;
+            v[0] = (_Float16)acc[fm][fn][q * 4 + 0];
+            v[1] = (_Float16)acc[fm][fn][q * 4 + 1];
+            v[2] = (_Float16)acc[fm][fn][q * 4 + 2];
+            v[3] = (_Float16)acc[fm][fn][q * 4 + 3];
+            *reinterpret_cast<half4*>(static_cast<_Float16*>(g.C) + m * N + n) = v;
+          }
         }
       }
     }
@@ -320,7 +325,12 @@ template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmArgs& a, bool out_f32, hipStream_t s) {
   const int64_t MB = (a.M + BM - 1) / BM;
   const int64_t NB = (a.N + BN - 1) / BN;
-  const dim3 grid((unsigned)(MB * NB));
+  // Persistent grid of at most one workgroup per CU. A running consumer then
+  // always leaves room on its CU (registers, LDS, wave slots) for producer
+  // workgroups, so spinning consumers can never lock the producer out.
+  const int64_t tiles = MB * NB;
+  const int64_t g = tiles < a.num_cus ? tiles : a.num_cus;
+  const dim3 grid((unsigned)g);
   const dim3 block(64 * WM * WN);
   const bool gated = a.gate.flags != nullptr;
   if (gated) {

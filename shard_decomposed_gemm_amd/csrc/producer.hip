@@ -60,31 +60,26 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
   const _Float16* __restrict__ src = a.src[s] + (int64_t)kt * a.bkf;
   _Float16* __restrict__ dst = a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * a.bkf;
 
-  constexpr int U = 4;
+  // Four 16-byte chunks in flight per thread (plain registers, no arrays).
+  auto src_at = [&](int64_t cc) {
+    return reinterpret_cast<const uint4*>(src + (r0 + cc / cpr) * a.KS + (cc % cpr) * 8);
+  };
+  auto dst_at = [&](int64_t cc) {
+    return reinterpret_cast<uint4*>(dst + (r0 + cc / cpr) * a.dst_ld + (cc % cpr) * 8);
+  };
+  constexpr int P = kProducerThreads;
   int64_t c = threadIdx.x;
-  for (; c + (U - 1) * kProducerThreads < total; c += U * kProducerThreads) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t cc = c + u * kProducerThreads;
-      const int64_t row = r0 + cc / cpr;
-      const int col = (int)(cc % cpr);
-      v[u] = *reinterpret_cast<const uint4*>(src + row * a.KS + col * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t cc = c + u * kProducerThreads;
-      const int64_t row = r0 + cc / cpr;
-      const int col = (int)(cc % cpr);
-      *reinterpret_cast<uint4*>(dst + row * a.dst_ld + col * 8) = v[u];
-    }
+  for (; c + 3 * P < total; c += 4 * P) {
+    const uint4 v0 = *src_at(c);
+    const uint4 v1 = *src_at(c + P);
+    const uint4 v2 = *src_at(c + 2 * P);
+    const uint4 v3 = *src_at(c + 3 * P);
+    *dst_at(c) = v0;
+    *dst_at(c + P) = v1;
+    *dst_at(c + 2 * P) = v2;
+    *dst_at(c + 3 * P) = v3;
   }
-  for (; c < total; c += kProducerThreads) {
-    const int64_t row = r0 + c / cpr;
-    const int col = (int)(c % cpr);
-    *reinterpret_cast<uint4*>(dst + row * a.dst_ld + col * 8) =
-        *reinterpret_cast<const uint4*>(src + row * a.KS + col * 8);
-  }
+  for (; c < total; c += P) *dst_at(c) = *src_at(c);
 
   if (a.flags) {
     // Make this thread's stores visible at agent scope, gather the workgroup,
