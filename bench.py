@@ -71,6 +71,23 @@ def cpu_baseline(W, M, K, N, budget_s: float):
             "seconds": t1}
 
 
+def calibrate_copy(steps: int):
+    """A plain device-to-device copy of 1 GiB: the known byte count (1 GiB read, 1 GiB
+    written per dispatch) against which FETCH_SIZE / WRITE_SIZE are scaled."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(max(1, steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(1, steps)
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "us_per_copy": dt * 1e6,
+                      "GBps_read_plus_write": 2 * n / dt / 1e9}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,7 +97,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy(args.steps)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the flag-gated path keeps all W inbox slots in one GPU's HBM "
               "and this build has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)

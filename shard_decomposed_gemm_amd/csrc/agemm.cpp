@@ -25,6 +25,8 @@ struct agemm_ctx {
   agemm_dtype c_dtype = AGEMM_F16;
   int device = 0;
   int num_cus = 0;
+  int tile_config = -1;  // AGEMM_TILE_CONFIG override of the MFMA tile choice
+  int strict_acquire = 0;  // AGEMM_STRICT_ACQUIRE=1: agent-scope acquire fence after flag waits
   double ticks_per_ns = 0.1;  // wall clock (kHz / 1e6)
   uint64_t timeout_ticks = 0;
 
@@ -34,7 +36,7 @@ struct agemm_ctx {
   uint64_t* t0_fused = nullptr;
   uint64_t* t0_bsp = nullptr;
   _Float16* gathered = nullptr;  // M x K, BSP only
-  float* ws = nullptr;           // small-M split-K workspace, T x M x N
+  float* ws = nullptr;           // small-M split-K workspace, W x M x N
   uint32_t* counters = nullptr;  // small-M column-block counters
   ErrWord* err_host = nullptr;
   ErrWord* err_dev = nullptr;
@@ -150,6 +152,7 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.KS = c->KS;
   g.W = c->W;
   g.num_cus = c->num_cus;
+  g.tile_config = c->tile_config;
   g.gate = gate;
   const bool f32 = c->c_dtype == AGEMM_F32;
   hipError_t e;
@@ -169,7 +172,6 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
 Gate no_gate(agemm_ctx* c) {
   Gate g{};
   g.flags = nullptr;
-  g.steps_per_tile = (int32_t)(c->bkf / 64);
   g.kt = c->kt;
   g.t = c->t;
   g.err = c->err_dev;
@@ -234,8 +236,9 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   c->kt = (int32_t)(KS / bkf);
   c->t = c->kt * W;
   c->c_dtype = c_dtype;
-  // Each producer workgroup copies about 64 KiB of one tile.
-  c->rows_per_item = (int32_t)std::max<int64_t>(1, 65536 / (bkf * 2));
+  // Each producer workgroup copies about 256 KiB of one tile (fewer, larger
+  // workgroups: each ends with one L2 write-back before its flag increment).
+  c->rows_per_item = (int32_t)std::max<int64_t>(1, 262144 / (bkf * 2));
   c->items_per_tile = (int32_t)((M + c->rows_per_item - 1) / c->rows_per_item);
 
   hipError_t e = hipGetDevice(&c->device);
@@ -253,14 +256,19 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     if (ms > 0) timeout_us = ms * 1000;
   }
   c->timeout_ticks = (uint64_t)((double)timeout_us * 1000.0 * c->ticks_per_ns);
+  if (const char* env = std::getenv("AGEMM_STRICT_ACQUIRE")) c->strict_acquire = std::atoi(env) != 0;
+  if (const char* env = std::getenv("AGEMM_TILE_CONFIG")) {
+    const int v = std::atoi(env);
+    if (v >= 0 && v < mfma_config_count()) c->tile_config = v;
+  }
 
   // Everything the context owns is allocated (and zeroed) here, so no call
   // on the hot path allocates or relies on an unordered memset.
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
   const size_t ctrl_bytes = sizeof(uint32_t) * kMaxTiles + 4 * sizeof(uint64_t);
-  const bool small = small_m_fits(M, bkf);
-  const size_t ws_bytes = small ? sizeof(float) * (size_t)c->t * (size_t)M * (size_t)N : 0;
+  const bool small = small_m_fits(M, KS);
+  const size_t ws_bytes = small ? sizeof(float) * (size_t)W * (size_t)M * (size_t)N : 0;
   const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)small_m_column_blocks(N) : 0;
   bool ok = hipMalloc(&c->inbox, inbox_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->gathered, gathered_bytes) == hipSuccess;
@@ -370,6 +378,7 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   gate.flags = ctx->flags;
   gate.target = ctx->epoch * (uint32_t)ctx->items_per_tile;  // wraps with the counters
   gate.timeout_ticks = ctx->timeout_ticks;
+  gate.strict = ctx->strict_acquire;
   rc = launch_gemm(ctx, src, gate, B, C, s);
   if (rc) return rc;
   ctx->consumed_this_epoch = true;

@@ -27,10 +27,10 @@ struct ASource {
 struct Gate {
   const uint32_t* flags;
   uint32_t target;          // epoch * contributors per tile (wrapping)
-  int32_t steps_per_tile;   // BKf / 64
   int32_t kt;               // KT
   int32_t t;                // T
   uint64_t timeout_ticks;   // wall-clock ticks (100 MHz on gfx950)
+  int32_t strict;           // 1: agent-scope acquire fence after each flag wait
   ErrWord* err;
 };
 
@@ -41,6 +41,7 @@ struct GemmArgs {
   int64_t M, N, K, KS;
   int32_t W;
   int32_t num_cus;    // compute units of the device (persistent grid size)
+  int32_t tile_config;  // MFMA tile configuration, -1 = chosen from the shape
   Gate gate;
 };
 
@@ -64,18 +65,19 @@ struct ProduceArgs {
   uint32_t offset_ticks[kMaxTiles]; // its release time after the launch's start, wall-clock ticks
 };
 
-// Split-K workspace for the small-M path.
+// Split-K workspace for the small-M path (one partial per shard).
 struct SmallMArgs {
   GemmArgs g;
-  float* ws;          // T x M x N partial sums
+  float* ws;          // W x M x N partial sums
   uint32_t* counters; // one per column block, zero between calls
 };
 
 hipError_t launch_produce(const ProduceArgs& a, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s);
+int mfma_config_count();
 hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s);
 int small_m_limit();
-bool small_m_fits(int64_t M, int64_t bkf);  // small-M kernel supports this shape
+bool small_m_fits(int64_t M, int64_t KS);  // small-M kernel supports this shape
 int64_t small_m_column_blocks(int64_t N);
 
 }  // namespace agemm

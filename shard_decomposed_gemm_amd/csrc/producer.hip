@@ -4,9 +4,9 @@
 // correctness check #4: a push kernel stores each tile of shard A_s into the
 // receive buffer Inbox(s, k) and only afterwards increments the tile's ready
 // counter Flags(s, k), so that a consumer that sees the increment also sees
-// the data. Here the inbox is in local HBM; the ordering is each thread's
-// agent-scope release fence, a workgroup barrier, then one agent-scope
-// release increment per workgroup. The same kernel with flags == nullptr is
+// the data. Here the inbox is in local HBM; the ordering is: every wave
+// waits for its stores, a workgroup barrier, then one agent-scope release
+// increment per workgroup. The same kernel with flags == nullptr is
 // the gather copy of the bulk-synchronous baseline (the all-gather that
 // concatenates [A_0 | ... | A_{W-1}] along K).
 //
@@ -82,9 +82,12 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
   for (; c < total; c += P) *dst_at(c) = *src_at(c);
 
   if (a.flags) {
-    // Make this thread's stores visible at agent scope, gather the workgroup,
-    // then publish the tile with one release increment.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Every wave waits until its stores have reached the L2 of its XCD, the
+    // workgroup meets, and one release increment (which writes that L2's dirty
+    // lines back before the flag changes) publishes the tile. One L2
+    // write-back per workgroup instead of one per wave: these serialise per
+    // XCD and cost microseconds when many workgroups issue them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
       __hip_atomic_fetch_add(a.flags + tile, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
