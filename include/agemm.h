@@ -26,7 +26,9 @@
  * tile id = s*KT + kt with KT = KS/BKf, T = W*KT tiles in all.
  *
  * Shapes accepted: 1 <= W <= 16, K % W == 0, KS % 64 == 0, N % 8 == 0,
- * N >= 8, 1 <= M <= 2^31-1, BKf a multiple of 64 that divides KS, T <= 64.
+ * 8 <= N <= 2^24, K <= 2^22, 1 <= M <= 2^31-1, BKf a multiple of 64 that
+ * divides KS, T <= 64. (The K and N bounds keep every per-lane load offset
+ * of the GEMM within 32 bits.)
  * Pointers: device pointers, 16-byte aligned. Streams are hipStream_t passed
  * as void* (NULL = the null stream).
  *
@@ -37,9 +39,10 @@
  * word and leaves C undefined; agemm_check() reports it after the caller has
  * synchronised.
  *
- * Ownership: the context owns the inbox (W x M x KS fp16), the flags (T
- * uint32 counters), the gathered-A buffer of the BSP path, the split-K
- * workspace and the error word. The caller owns A_s, B, C and all streams.
+ * Ownership: the context owns two inboxes (each W x M x KS fp16, used by
+ * alternate epochs) with their flags (T uint32 counters each), the
+ * gathered-A buffer of the BSP path, the split-K workspace and the error
+ * word. The caller owns A_s, B, C and all streams.
  * A context is not thread-safe; use one per host thread.
  */
 #ifndef AGEMM_H
@@ -91,8 +94,10 @@ int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
  * raises Flags(s, kt), for every tile, in the schedule's order and at its
  * times (sched == NULL: shard order, no delay). a_shards: host array of W
  * device pointers, each M x KS fp16. Starts a new epoch: the next run_fused
- * waits for this call's flags. Before it overwrites the inbox, the producer
- * stream waits (device side) for the last run_fused on the previous epoch. */
+ * waits for this call's flags. Epochs alternate between the two inboxes:
+ * before it overwrites its inbox, the producer stream waits (device side)
+ * for the last run_fused of the epoch before the previous one, so a
+ * producer may fill its inbox while the previous epoch's consumer runs. */
 int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_schedule* sched, void* stream);
 
 /* Flag-gated consumer: C = sum_s Inbox(s) . B_s, waiting on Flags(s, kt)

@@ -30,9 +30,12 @@ struct agemm_ctx {
   double ticks_per_ns = 0.1;  // wall clock (kHz / 1e6)
   uint64_t timeout_ticks = 0;
 
-  _Float16* inbox = nullptr;     // W slots of M x KS
-  uint32_t* ctrl = nullptr;      // flags[64] | t0 fused[2] (u64) | t0 bsp[2] (u64)
-  uint32_t* flags = nullptr;
+  // Two inboxes, used by alternate epochs, each with its own flags: the
+  // producer of epoch e only has to wait for the consumers of epoch e-2, so it
+  // can fill its inbox while the consumer of epoch e-1 is still running.
+  _Float16* inbox[2] = {nullptr, nullptr};  // each W slots of M x KS
+  uint32_t* ctrl = nullptr;      // flags[2][64] | t0 fused[2] (u64) | t0 bsp[2] (u64)
+  uint32_t* flags[2] = {nullptr, nullptr};
   uint64_t* t0_fused = nullptr;
   uint64_t* t0_bsp = nullptr;
   _Float16* gathered = nullptr;  // M x K, BSP only
@@ -42,12 +45,15 @@ struct agemm_ctx {
   ErrWord* err_dev = nullptr;
 
   int32_t rows_per_item = 1, items_per_tile = 1;
-  uint32_t epoch = 0;            // produce calls so far
+  uint32_t epoch = 0;            // produce calls so far; epoch e uses inbox e & 1
+  uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox so far
   uint32_t parity_fused = 0, parity_bsp = 0;
 
   hipEvent_t ev_consumer = nullptr;  // after the last consumer call (fused, bsp or pull)
   hipEvent_t ev_producer = nullptr;  // after the last produce call
+  hipEvent_t ev_fused[2] = {nullptr, nullptr};  // after the last fused consumer of each inbox
   bool consumer_pending = false, producer_pending = false;
+  bool fused_pending[2] = {false, false};
   bool consumed_this_epoch = false;
 
   std::string last_error;
@@ -179,7 +185,7 @@ Gate no_gate(agemm_ctx* c) {
 }
 
 void free_all(agemm_ctx* c) {
-  if (c->inbox) hipFree(c->inbox);
+  if (c->inbox[0]) hipFree(c->inbox[0]);
   if (c->ctrl) hipFree(c->ctrl);
   if (c->gathered) hipFree(c->gathered);
   if (c->ws) hipFree(c->ws);
@@ -187,6 +193,8 @@ void free_all(agemm_ctx* c) {
   if (c->err_host) hipHostFree(c->err_host);
   if (c->ev_consumer) hipEventDestroy(c->ev_consumer);
   if (c->ev_producer) hipEventDestroy(c->ev_producer);
+  for (int i = 0; i < 2; ++i)
+    if (c->ev_fused[i]) hipEventDestroy(c->ev_fused[i]);
 }
 
 }  // namespace
@@ -211,7 +219,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   if (K % W) return AGEMM_ESHAPE;
   const int64_t KS = K / W;
   if (KS % 64 || N % 8) return AGEMM_ESHAPE;
-  if (K > INT32_MAX || N > INT32_MAX) return AGEMM_ESHAPE;
+  if (K > (int64_t{1} << 22) || N > (int64_t{1} << 24)) return AGEMM_ESHAPE;  // 32-bit lane offsets
   int64_t bkf = flag_ktile;
   if (bkf == 0) {
     bkf = std::min<int64_t>(256, KS);
@@ -266,11 +274,11 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   // on the hot path allocates or relies on an unordered memset.
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
-  const size_t ctrl_bytes = sizeof(uint32_t) * kMaxTiles + 4 * sizeof(uint64_t);
+  const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 4 * sizeof(uint64_t);
   const bool small = small_m_fits(M, KS);
   const size_t ws_bytes = small ? sizeof(float) * (size_t)W * (size_t)M * (size_t)N : 0;
   const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)small_m_column_blocks(N) : 0;
-  bool ok = hipMalloc(&c->inbox, inbox_bytes) == hipSuccess;
+  bool ok = hipMalloc(&c->inbox[0], 2 * inbox_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->gathered, gathered_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->ctrl, ctrl_bytes) == hipSuccess;
   if (ok && small) {
@@ -283,8 +291,10 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     delete c;
     return AGEMM_ENOMEM;
   }
-  c->flags = c->ctrl;
-  c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + kMaxTiles);
+  c->inbox[1] = c->inbox[0] + inbox_bytes / sizeof(_Float16);
+  c->flags[0] = c->ctrl;
+  c->flags[1] = c->ctrl + kMaxTiles;
+  c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + 2 * kMaxTiles);
   c->t0_bsp = c->t0_fused + 2;
   void* hp = nullptr;
   e = hipMemset(c->ctrl, 0, ctrl_bytes);
@@ -298,6 +308,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_consumer, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_fused[i], hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     free_all(c);
@@ -340,17 +351,18 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   rc = fill_schedule(ctx, sched, pa);
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The inbox may be overwritten only after the consumers of the previous
-  // epoch are done with it, and producers of successive epochs run in order.
+  // This epoch's inbox may be overwritten only once the fused consumers that
+  // last read it (two epochs ago) are done; producers run in order.
+  const int slot = (int)((ctx->epoch + 1) & 1u);
   hipError_t e = hipSuccess;
-  if (ctx->consumer_pending) e = hipStreamWaitEvent(s, ctx->ev_consumer, 0);
+  if (ctx->fused_pending[slot]) e = hipStreamWaitEvent(s, ctx->ev_fused[slot], 0);
   if (e == hipSuccess && ctx->producer_pending) e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_produce_args(ctx, a_shards, pa);
-  pa.dst = ctx->inbox;
+  pa.dst = ctx->inbox[slot];
   pa.dst_shard_stride = ctx->M * ctx->KS;
   pa.dst_ld = ctx->KS;
-  pa.flags = ctx->flags;
+  pa.flags = ctx->flags[slot];
   pa.t0 = ctx->t0_fused;
   pa.parity = ctx->parity_fused & 1u;
   e = launch_produce(pa, s);
@@ -360,6 +372,7 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   ctx->producer_pending = true;
   ctx->epoch++;
+  ctx->slot_epochs[slot]++;
   ctx->consumed_this_epoch = false;
   return AGEMM_OK;
 }
@@ -371,17 +384,22 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = order_after_consumer(ctx, s);
   if (rc) return rc;
+  const int slot = (int)(ctx->epoch & 1u);
   ASource src{};
-  for (int i = 0; i < kMaxShards; ++i) src.base[i] = i < ctx->W ? ctx->inbox + (int64_t)i * ctx->M * ctx->KS : nullptr;
+  for (int i = 0; i < kMaxShards; ++i)
+    src.base[i] = i < ctx->W ? ctx->inbox[slot] + (int64_t)i * ctx->M * ctx->KS : nullptr;
   src.lda = ctx->KS;
   Gate gate = no_gate(ctx);
-  gate.flags = ctx->flags;
-  gate.target = ctx->epoch * (uint32_t)ctx->items_per_tile;  // wraps with the counters
+  gate.flags = ctx->flags[slot];
+  gate.target = ctx->slot_epochs[slot] * (uint32_t)ctx->items_per_tile;  // wraps with the counters
   gate.timeout_ticks = ctx->timeout_ticks;
   gate.strict = ctx->strict_acquire;
   rc = launch_gemm(ctx, src, gate, B, C, s);
   if (rc) return rc;
   ctx->consumed_this_epoch = true;
+  hipError_t e = hipEventRecord(ctx->ev_fused[slot], s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+  ctx->fused_pending[slot] = true;
   return mark_consumer(ctx, s);
 }
 

@@ -44,6 +44,8 @@ def test_status_strings():
     (8, 1, 8 * 96, 256, agemm.ESHAPE),  # K/W not a multiple of 64
     (8, 1, 512, 250, agemm.ESHAPE),     # N not a multiple of 8
     (8, 1, 512, 0, agemm.ESHAPE),
+    (8, 1, (1 << 22) + 8 * 64, 256, agemm.ESHAPE),  # K past the 32-bit lane-offset bound
+    (8, 1, 512, (1 << 24) + 8, agemm.ESHAPE),       # N past the 32-bit lane-offset bound
 ])
 def test_create_rejects_bad_shapes_without_gpu(W, M, K, N, code):
     lib = agemm.load()

@@ -28,14 +28,15 @@ def gate_mode(request, monkeypatch):
 
 @pytest.mark.parametrize("W,M,K,N", [(8, 1, 2048, 1024), (8, 4, 4096, 2056), (8, 96, 2048, 1024), (8, 512, 2048, 1024)])
 def test_poisoned_inbox_is_never_read_early(W, M, K, N, gate_mode):
-    """Epoch 1 fills the inbox with NaN; epoch 2 releases real tiles late and out of
-    order while the consumer is already running. Any premature read would show NaN."""
+    """Epochs 1 and 2 fill both inboxes with NaN; epoch 3 releases real tiles late and
+    out of order while the consumer is already running. Any premature read would show NaN."""
     import torch
     a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=41)
     ref = oracle.sharded_gemm(sh, b)
     ctx = _ctx(W, M, K, N, "f32")
     nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
     ctx.produce(nan)
+    ctx.produce(nan)  # epochs alternate between two inboxes: poison both
     torch.cuda.synchronize()
     order, offs = synth.schedule(0x5100 + M, ctx.t, 40_000)  # up to 40 us between releases
     sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
@@ -51,17 +52,18 @@ def test_poisoned_inbox_is_never_read_early(W, M, K, N, gate_mode):
 
 @pytest.mark.parametrize("M", [1, 256])
 def test_alternating_epochs(M, gate_mode):
-    """Two data sets alternate over successive epochs on two streams; each epoch's C
-    must match its own data (the inbox is not overwritten while still being read)."""
+    """Three data sets cycle over successive epochs on two streams (so each of the two
+    inboxes holds a different data set every time it is reused); each epoch's C must
+    match its own data (an inbox is not overwritten while still being read)."""
     import torch
     W, K, N = 8, 2048, 1024
-    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (51, 52)]
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (51, 52, 53)]
     refs = [oracle.sharded_gemm(p[1], p[2]) for p in probs]
     ctx = _ctx(W, M, K, N, "f32")
     sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for e in range(6):
-        p = probs[e % 2]
+        p = probs[e % 3]
         C = gu.empty_c(M, N, "f32")
         order, offs = synth.schedule(0x5200 + e, ctx.t, 5_000 if e % 3 == 0 else 0)
         ctx.produce(p[3], schedule=(order, offs), stream=sp)
@@ -70,7 +72,7 @@ def test_alternating_epochs(M, gate_mode):
     torch.cuda.synchronize()
     ctx.check()
     for e, C in enumerate(outs):
-        assert np.abs(gu.c_to_f64(C) - refs[e % 2]).max() <= oracle.tolerance(K), e
+        assert np.abs(gu.c_to_f64(C) - refs[e % 3]).max() <= oracle.tolerance(K), e
 
 
 @pytest.mark.parametrize("M", [2, 300])
@@ -147,13 +149,13 @@ def test_call_order_and_argument_errors():
 
 @pytest.mark.parametrize("M", [1, 7, 300, 1024])
 def test_epoch_stress_bitwise(M, gate_mode):
-    """120 epochs alternate two data sets with jittered release schedules while the
+    """120 epochs cycle three data sets with jittered release schedules while the
     consumer runs concurrently. Each epoch's C must equal, bit for bit, the ungated
-    (pull) result of its own data set: a read of the previous epoch's inbox content
-    would change it."""
+    (pull) result of its own data set: a read of an inbox's previous content (another
+    data set, since three sets cycle over two inboxes) would change it."""
     import torch
     W, K, N = 8, 2048, 1544
-    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (81, 82)]
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (81, 82, 83)]
     ctx = _ctx(W, M, K, N, "f16")
     refs = []
     for p in probs:
@@ -167,7 +169,7 @@ def test_epoch_stress_bitwise(M, gate_mode):
     outs = [gu.empty_c(M, N, "f16") for _ in range(4)]
     bad = []
     for e in range(120):
-        p = probs[e % 2]
+        p = probs[e % 3]
         order, offs = synth.schedule(0x5300 + e, ctx.t, (e % 5) * 3_000)
         C = outs[e % 4]
         ctx.produce(p[3], schedule=(order, offs), stream=sp)
@@ -175,7 +177,7 @@ def test_epoch_stress_bitwise(M, gate_mode):
         if e % 4 == 3:
             torch.cuda.synchronize()
             for j in range(4):
-                if not torch.equal(outs[j].view(torch.int16), refs[(e - 3 + j) % 2].view(torch.int16)):
+                if not torch.equal(outs[j].view(torch.int16), refs[(e - 3 + j) % 3].view(torch.int16)):
                     bad.append(e - 3 + j)
     torch.cuda.synchronize()
     ctx.check()

@@ -139,3 +139,24 @@ def test_structural_closed_forms(M):
     C3 = gu.empty_c(M, N, "f32")
     _run(ctx, "fused", [torch.zeros((M, KS), dtype=torch.float16, device=gu.dev()) for _ in range(W)], B, C3)
     assert not C3.cpu().numpy().any()
+
+
+@pytest.mark.parametrize("tile_config", [0, 1, 2, 3])
+@pytest.mark.parametrize("W,M,K,N", [(8, 300, 2048, 1032), (4, 520, 1024, 264)])
+def test_every_tile_config(tile_config, W, M, K, N, monkeypatch):
+    """Each MFMA tile configuration (chosen at create time through AGEMM_TILE_CONFIG),
+    gated with the producer running concurrently, ungated (pull) and BSP, on ragged
+    shapes: exact inputs, so fused, BSP and pull must agree bit for bit with the oracle."""
+    monkeypatch.setenv("AGEMM_TILE_CONFIG", str(tile_config))
+    a = gu.coarse_bits(0xE000 + M, M, K)
+    b = gu.coarse_bits(0xE100 + N, K, N)
+    sh = synth.shards(a, W)
+    ref = oracle.sharded_gemm(sh, b)
+    dsh = [gu.to_dev(s) for s in sh]
+    B = gu.to_dev(b)
+    ctx = _ctx(W, M, K, N, "f32")
+    order, offs = synth.schedule(0xE200 + tile_config, ctx.t, 10_000)
+    for path in ("fused", "pull", "bsp"):
+        C = gu.empty_c(M, N, "f32")
+        _run(ctx, path, dsh, B, C, schedule=(order, offs) if path != "pull" else None)
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), (tile_config, path)
