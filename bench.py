@@ -16,6 +16,7 @@ Prints one JSON line. Besides the required fields it carries:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +38,38 @@ WORKLOADS = {
 # MI355X published peaks
 PEAK_FP16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+
+
+CSRC = os.path.join(ROOT, "shard_decomposed_gemm_amd", "csrc")
+KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "agemm_internal.h"), "small_m": ("gemm_small_m.hip", "agemm_internal.h")}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "consumer_hbm_traffic.md")
+
+
+def kernel_digest(kind: str) -> str:
+    """Digest of the consumer kernel's sources: counter figures taken from another
+    version of the kernel are not reported."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per launch of the consumer kernel, from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size); None if there is
+    none for this workload or the kernel has changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = kernel_digest(kind)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[1:] if "=" in x)
+            if kv.get("workload") == workload and kv.get("digest") == digest:
+                return float(kv["bytes_per_launch"])
+    return None
 
 
 def algorithmic(W, M, K, N, c_bytes):
@@ -97,6 +130,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="producer and consumer on one stream (the consumer then finds every flag up); "
+                         "for counter collection, which serialises kernel dispatches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -129,6 +165,8 @@ def main():
     ctx = Context(W, M, K, N, c_dtype=c_dtype)
     sched = synth.schedule(0x5005, ctx.t, 20_000) if sched_kind == "random" else None
     sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    if args.one_stream:
+        sp = sc
     torch.cuda.synchronize()
 
     def fused_step(i):
@@ -176,7 +214,11 @@ def main():
         achieved = cons_bytes / (kavg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None}
-    roof["kernel"] = "consumer GEMM (flag-gated)"
+    kind, tile_cfg = ctx.consumer
+    roof["traffic"] = measured_traffic(args.workload, kind)
+    roof["kernel"] = ("flag-gated MFMA tile GEMM, tile config %d" % tile_cfg if kind == "mfma"
+                      else "flag-gated small-M split-K streaming GEMM")
+    roof["kernel_digest"] = kernel_digest(kind)
     roof["algorithmic_bytes_per_launch"] = cons_bytes
     roof["flops_per_launch"] = flops
     roof["kernel_us_avg"] = kavg * 1e3

@@ -90,6 +90,12 @@ int agemm_destroy(agemm_ctx* ctx);
 /* Shape queries: BKf, KT = KS/BKf and T = W*KT (any output pointer may be NULL). */
 int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
 
+/* Consumer kernel the context's GEMM calls launch: *kind = 0 for the MFMA
+ * tile kernel (then *tile_config is its tile configuration, 0..3), 1 for the
+ * small-M split-K streaming kernel (M <= 8; *tile_config = -1). Either output
+ * pointer may be NULL. */
+int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_config);
+
 /* Producer (Push model): copies tile (s, kt) of A_s into Inbox(s) and then
  * raises Flags(s, kt), for every tile, in the schedule's order and at its
  * times (sched == NULL: shard order, no delay). a_shards: host array of W

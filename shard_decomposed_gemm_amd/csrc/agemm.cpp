@@ -39,7 +39,8 @@ struct agemm_ctx {
   uint64_t* t0_fused = nullptr;
   uint64_t* t0_bsp = nullptr;
   _Float16* gathered = nullptr;  // M x K, BSP only
-  float* ws = nullptr;           // small-M split-K workspace, W x M x N
+  SmallMPlan small_plan;         // small-M work split (small_plan.ok: the small-M kernel is used)
+  float* ws = nullptr;           // small-M split-K workspace, ranges x M x N
   uint32_t* counters = nullptr;  // small-M column-block counters
   ErrWord* err_host = nullptr;
   ErrWord* err_dev = nullptr;
@@ -49,9 +50,15 @@ struct agemm_ctx {
   uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox so far
   uint32_t parity_fused = 0, parity_bsp = 0;
 
-  hipEvent_t ev_consumer = nullptr;  // after the last consumer call (fused, bsp or pull)
+  // Ordering between calls on different streams. One event is recorded per
+  // call; a wait is skipped when the event was recorded on the waiting
+  // stream (in-stream order already holds, and every dependency packet costs
+  // command-processor time between kernels).
+  hipEvent_t ev_consumer = nullptr;  // after the last BSP or pull consumer call
   hipEvent_t ev_producer = nullptr;  // after the last produce call
   hipEvent_t ev_fused[2] = {nullptr, nullptr};  // after the last fused consumer of each inbox
+  hipEvent_t last_consumer_ev = nullptr;        // the event of the last consumer call, whichever
+  hipStream_t consumer_stream = nullptr, producer_stream = nullptr, fused_stream[2] = {nullptr, nullptr};
   bool consumer_pending = false, producer_pending = false;
   bool fused_pending[2] = {false, false};
   bool consumed_this_epoch = false;
@@ -132,16 +139,19 @@ void base_produce_args(agemm_ctx* c, const void* const* a_shards, ProduceArgs& p
 // Orders a new consumer after the previous one (they share the workspace and,
 // for BSP, the gathered buffer) when they are on different streams.
 int order_after_consumer(agemm_ctx* c, hipStream_t s) {
-  if (c->consumer_pending) {
-    hipError_t e = hipStreamWaitEvent(s, c->ev_consumer, 0);
+  if (c->consumer_pending && c->consumer_stream != s) {
+    hipError_t e = hipStreamWaitEvent(s, c->last_consumer_ev, 0);
     if (e != hipSuccess) return hip_fail(c, e, "hipStreamWaitEvent");
   }
   return AGEMM_OK;
 }
 
-int mark_consumer(agemm_ctx* c, hipStream_t s) {
-  hipError_t e = hipEventRecord(c->ev_consumer, s);
+// Records `ev` after a consumer call on stream s.
+int mark_consumer(agemm_ctx* c, hipStream_t s, hipEvent_t ev) {
+  hipError_t e = hipEventRecord(ev, s);
   if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+  c->last_consumer_ev = ev;
+  c->consumer_stream = s;
   c->consumer_pending = true;
   return AGEMM_OK;
 }
@@ -165,6 +175,7 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   if (c->ws) {
     SmallMArgs sa{};
     sa.g = g;
+    sa.plan = c->small_plan;
     sa.ws = c->ws;
     sa.counters = c->counters;
     e = launch_gemm_small_m(sa, f32, s);
@@ -275,9 +286,17 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
   const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 4 * sizeof(uint64_t);
-  const bool small = small_m_fits(M, KS);
-  const size_t ws_bytes = small ? sizeof(float) * (size_t)W * (size_t)M * (size_t)N : 0;
-  const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)small_m_column_blocks(N) : 0;
+  c->small_plan = small_m_plan(W, M, KS, N, c->num_cus);
+  if (const char* env = std::getenv("AGEMM_SMALL_M_PLAN")) {  // "lanes,ranges,wg_per_cu" override
+    int l = 0, r = 0, wpc = 0;
+    if (std::sscanf(env, "%d,%d,%d", &l, &r, &wpc) == 3 && c->small_plan.ok) {
+      const SmallMPlan p = small_m_plan_with(W, M, KS, N, l, r, wpc);
+      if (p.ok) c->small_plan = p;
+    }
+  }
+  const bool small = c->small_plan.ok;
+  const size_t ws_bytes = small ? sizeof(float) * (size_t)c->small_plan.ranges * (size_t)M * (size_t)N : 0;
+  const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)c->small_plan.nblk : 0;
   bool ok = hipMalloc(&c->inbox[0], 2 * inbox_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->gathered, gathered_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->ctrl, ctrl_bytes) == hipSuccess;
@@ -336,6 +355,14 @@ int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t) {
   return AGEMM_OK;
 }
 
+int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_config) {
+  if (!ctx) return AGEMM_EINVAL;
+  const bool small = ctx->ws != nullptr;
+  if (kind) *kind = small ? 1 : 0;
+  if (tile_config) *tile_config = small ? -1 : mfma_config_for(ctx->M, ctx->tile_config);
+  return AGEMM_OK;
+}
+
 int agemm_set_spin_timeout_us(agemm_ctx* ctx, int64_t us) {
   if (!ctx) return AGEMM_EINVAL;
   if (us < 1) return fail(ctx, AGEMM_EINVAL, "timeout must be positive");
@@ -355,8 +382,9 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   // last read it (two epochs ago) are done; producers run in order.
   const int slot = (int)((ctx->epoch + 1) & 1u);
   hipError_t e = hipSuccess;
-  if (ctx->fused_pending[slot]) e = hipStreamWaitEvent(s, ctx->ev_fused[slot], 0);
-  if (e == hipSuccess && ctx->producer_pending) e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
+  if (ctx->fused_pending[slot] && ctx->fused_stream[slot] != s) e = hipStreamWaitEvent(s, ctx->ev_fused[slot], 0);
+  if (e == hipSuccess && ctx->producer_pending && ctx->producer_stream != s)
+    e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_produce_args(ctx, a_shards, pa);
   pa.dst = ctx->inbox[slot];
@@ -371,6 +399,7 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   e = hipEventRecord(ctx->ev_producer, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   ctx->producer_pending = true;
+  ctx->producer_stream = s;
   ctx->epoch++;
   ctx->slot_epochs[slot]++;
   ctx->consumed_this_epoch = false;
@@ -397,10 +426,11 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   rc = launch_gemm(ctx, src, gate, B, C, s);
   if (rc) return rc;
   ctx->consumed_this_epoch = true;
-  hipError_t e = hipEventRecord(ctx->ev_fused[slot], s);
-  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+  rc = mark_consumer(ctx, s, ctx->ev_fused[slot]);
+  if (rc) return rc;
   ctx->fused_pending[slot] = true;
-  return mark_consumer(ctx, s);
+  ctx->fused_stream[slot] = s;
+  return AGEMM_OK;
 }
 
 int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, const agemm_schedule* sched,
@@ -437,7 +467,7 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   src.lda = ctx->K;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
-  return mark_consumer(ctx, s);
+  return mark_consumer(ctx, s, ctx->ev_consumer);
 }
 
 int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, void* stream) {
@@ -453,7 +483,7 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
   src.lda = ctx->KS;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
-  return mark_consumer(ctx, s);
+  return mark_consumer(ctx, s, ctx->ev_consumer);
 }
 
 int agemm_check(agemm_ctx* ctx) {
@@ -464,7 +494,7 @@ int agemm_check(agemm_ctx* ctx) {
   w->code = 0;
   // A timed-out small-M launch leaves its column counters part-way; clear them.
   if (ctx->counters) {
-    hipError_t e = hipMemset(ctx->counters, 0, sizeof(uint32_t) * (size_t)small_m_column_blocks(ctx->N));
+    hipError_t e = hipMemset(ctx->counters, 0, sizeof(uint32_t) * (size_t)ctx->small_plan.nblk);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemset(counters)");
   }

@@ -65,19 +65,33 @@ struct ProduceArgs {
   uint32_t offset_ticks[kMaxTiles]; // its release time after the launch's start, wall-clock ticks
 };
 
-// Split-K workspace for the small-M path (one partial per shard).
+// Work split of the small-M path, chosen on the host for the device's CU
+// count: items are (K-range, column block), a K-range being `ranges`-th of the
+// shards and a column block 8 * lanes columns.
+struct SmallMPlan {
+  int32_t lanes = 0;   // active lanes per streaming wave (8 columns each)
+  int32_t ranges = 0;  // K-ranges (divides W)
+  int32_t nblk = 0;    // column blocks
+  int32_t wg_per_cu = 1;  // cap of the persistent grid, in workgroups per CU
+  bool ok = false;     // the small-M kernel takes this shape
+};
+
+// Split-K workspace for the small-M path (one partial per K-range).
 struct SmallMArgs {
   GemmArgs g;
-  float* ws;          // W x M x N partial sums
+  SmallMPlan plan;
+  float* ws;          // ranges x M x N partial sums
   uint32_t* counters; // one per column block, zero between calls
 };
 
 hipError_t launch_produce(const ProduceArgs& a, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s);
 int mfma_config_count();
+int mfma_config_for(int64_t M, int tile_config);  // configuration launch_gemm_mfma uses
 hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s);
 int small_m_limit();
-bool small_m_fits(int64_t M, int64_t KS);  // small-M kernel supports this shape
-int64_t small_m_column_blocks(int64_t N);
+SmallMPlan small_m_plan(int W, int64_t M, int64_t KS, int64_t N, int num_cus);
+// The plan for given lanes / ranges / workgroups per CU, if the kernel takes it.
+SmallMPlan small_m_plan_with(int W, int64_t M, int64_t KS, int64_t N, int lanes, int ranges, int wg_per_cu);
 
 }  // namespace agemm

@@ -518,10 +518,13 @@ hipError_t launch_cfg(const GemmArgs& a, bool out_f32, hipStream_t s) {
 
 int mfma_config_count() { return 4; }
 
+int mfma_config_for(int64_t M, int tile_config) {
+  if (tile_config >= 0 && tile_config < mfma_config_count()) return tile_config;
+  return M > 192 ? 0 : 2;
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s) {
-  int cfg = a.tile_config;
-  if (cfg < 0) cfg = a.M > 192 ? 0 : 2;
-  switch (cfg) {
+  switch (mfma_config_for(a.M, a.tile_config)) {
     case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, out_f32, s);   // 4 waves, 128x128 per wave
     case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, out_f32, s);   // 8 waves, 128x64 per wave
     case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, out_f32, s);   // 4 waves, 64x64 per wave
