@@ -360,6 +360,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   const uint32_t lds0 = lds_addr(smem);
   Frags<FM, FN> F0, F1;
 
+  // First look at the flags with plain loads, which the per-XCD L2 serves
+  // after one miss: a device-coherent poll from every wave of the grid would
+  // queue a thousand requests on one memory line at launch. A cached flag can
+  // only lag the true value (flags only grow within the wrap window), so a
+  // flag seen raised here is raised; one seen down is polled coherently by
+  // the gate when it is needed.
+  if constexpr (GATED) {
+    bool up = false;
+    if (lane < g.gate.t) up = (int32_t)(g.gate.flags[lane] - g.gate.target) >= 0;
+    const uint64_t mask = __ballot(up);
+    ready = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32)) << 32) |
+            (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)mask);
+    if (g.gate.strict) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    asm volatile("" ::: "memory");
+  }
+
   // Prologue: steps 0 .. STAGES-2 in full; the interval opened by the
   // prologue barrier then loads step STAGES-1 into the last buffer.
   cursor_enter(cw);

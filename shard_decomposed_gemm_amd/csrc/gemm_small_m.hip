@@ -188,12 +188,11 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(SmallMArgs sa) {
     // the range's A is staged and the stream runs without a single wait.
     fetch(X, 0);
     if constexpr (GATED) {
+      // Plain loads (served by the L2 after one miss; see the MFMA consumer):
+      // a cached flag can only lag, so "all up" is safe to trust, and any
+      // flag seen down is then waited for with device-coherent polls.
       bool up = true;
-      if (lane < tiles) {
-        const uint32_t v = __hip_atomic_load(const_cast<uint32_t*>(g.gate.flags) + s0 * KT + lane, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        up = (int32_t)(v - g.gate.target) >= 0;
-      }
+      if (lane < tiles) up = (int32_t)(g.gate.flags[s0 * KT + lane] - g.gate.target) >= 0;
       if (__ballot(!up) != 0) {
         for (int i = 0; i < tiles; ++i) wait_flag(s0 * KT + i);
       }

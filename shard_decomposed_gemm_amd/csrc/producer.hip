@@ -4,11 +4,16 @@
 // correctness check #4: a push kernel stores each tile of shard A_s into the
 // receive buffer Inbox(s, k) and only afterwards increments the tile's ready
 // counter Flags(s, k), so that a consumer that sees the increment also sees
-// the data. Here the inbox is in local HBM; the ordering is: every wave
-// waits for its stores, a workgroup barrier, then one agent-scope release
-// increment per workgroup. The same kernel with flags == nullptr is
-// the gather copy of the bulk-synchronous baseline (the all-gather that
-// concatenates [A_0 | ... | A_{W-1}] along K).
+// the data. Here the inbox is in local HBM. The inbox stores are
+// device-coherent (agent-scope atomic stores, which go past the per-XCD L2 to
+// the coherence point), every thread waits until they have completed, the
+// workgroup meets, and one relaxed increment per workgroup raises the flag.
+// An agent-scope release increment would instead write back the whole L2 of
+// the producer's XCD, including the consumer's dirty C lines, once per
+// workgroup. The same kernel with flags == nullptr is the gather copy of the
+// bulk-synchronous baseline (the all-gather that concatenates
+// [A_0 | ... | A_{W-1}] along K), with plain stores: the kernel boundary
+// publishes them.
 //
 // One workgroup = one work item = rows [q*R, (q+1)*R) of tile (s, kt), with
 // items ordered by release position p. A release schedule makes the item
@@ -24,6 +29,7 @@ constexpr int kProducerThreads = 256;
 
 __device__ inline uint64_t wall_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
+template <bool FLAGS>
 __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a) {
   const int item = blockIdx.x;
   const int p = item / a.items_per_tile;
@@ -67,6 +73,15 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
   auto dst_at = [&](int64_t cc) {
     return reinterpret_cast<uint4*>(dst + (r0 + cc / cpr) * a.dst_ld + (cc % cpr) * 8);
   };
+  auto put = [&](int64_t cc, const uint4& v) {
+    if constexpr (FLAGS) {
+      uint64_t* d = reinterpret_cast<uint64_t*>(dst_at(cc));
+      __hip_atomic_store(d, ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(d + 1, ((uint64_t)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *dst_at(cc) = v;
+    }
+  };
   constexpr int P = kProducerThreads;
   int64_t c = threadIdx.x;
   for (; c + 3 * P < total; c += 4 * P) {
@@ -74,23 +89,19 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
     const uint4 v1 = *src_at(c + P);
     const uint4 v2 = *src_at(c + 2 * P);
     const uint4 v3 = *src_at(c + 3 * P);
-    *dst_at(c) = v0;
-    *dst_at(c + P) = v1;
-    *dst_at(c + 2 * P) = v2;
-    *dst_at(c + 3 * P) = v3;
+    put(c, v0);
+    put(c + P, v1);
+    put(c + 2 * P, v2);
+    put(c + 3 * P, v3);
   }
-  for (; c < total; c += P) *dst_at(c) = *src_at(c);
+  for (; c < total; c += P) put(c, *src_at(c));
 
-  if (a.flags) {
-    // Every wave waits until its stores have reached the L2 of its XCD, the
-    // workgroup meets, and one release increment (which writes that L2's dirty
-    // lines back before the flag changes) publishes the tile. One L2
-    // write-back per workgroup instead of one per wave: these serialise per
-    // XCD and cost microseconds when many workgroups issue them.
+  if constexpr (FLAGS) {
+    // Every thread's device-coherent stores have completed before the
+    // workgroup meets; then one increment publishes the tile.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(a.flags + tile, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.flags + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -98,7 +109,8 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
 
 hipError_t launch_produce(const ProduceArgs& a, hipStream_t s) {
   const unsigned items = (unsigned)a.t * (unsigned)a.items_per_tile;
-  hipLaunchKernelGGL(produce_kernel, dim3(items), dim3(kProducerThreads), 0, s, a);
+  if (a.flags) hipLaunchKernelGGL(produce_kernel<true>, dim3(items), dim3(kProducerThreads), 0, s, a);
+  else hipLaunchKernelGGL(produce_kernel<false>, dim3(items), dim3(kProducerThreads), 0, s, a);
   return hipGetLastError();
 }
 
