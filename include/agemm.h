@@ -126,6 +126,18 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
  * the AGEMM_SPIN_TIMEOUT_MS environment variable at create time). */
 int agemm_set_spin_timeout_us(agemm_ctx* ctx, int64_t us);
 
+/* Kernel timing. agemm_timing_begin allocates (or reuses) max_launches
+ * pairs of HIP events; every consumer kernel launched by run_fused, run_bsp
+ * or run_pull after it (up to max_launches) carries a pair attached to its
+ * own dispatch, so the interval is that kernel's execution on the device
+ * (the stamps a kernel-trace profiler reports), not the surrounding stream
+ * activity. agemm_timing_end synchronises on those events and writes the
+ * durations in microseconds, in launch order, to us[0 .. min(count, max)-1]
+ * (us may be NULL); *count receives the number of timed launches.
+ * ESTATE if begin is called twice or end without begin. */
+int agemm_timing_begin(agemm_ctx* ctx, int32_t max_launches);
+int agemm_timing_end(agemm_ctx* ctx, float* us, int32_t max, int32_t* count);
+
 /* After the caller has synchronised: AGEMM_ETIMEOUT if a consumer timed out
  * since the last check (the error word is then cleared), else AGEMM_OK. */
 int agemm_check(agemm_ctx* ctx);

@@ -20,7 +20,8 @@ F16, F32 = 0, 1
 
 EXPORTED = (
     "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_produce", "agemm_run_fused",
-    "agemm_run_bsp", "agemm_run_pull", "agemm_set_spin_timeout_us", "agemm_check",
+    "agemm_run_bsp", "agemm_run_pull", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
+    "agemm_check",
     "agemm_last_error", "agemm_status_string",
 )
 
@@ -56,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.agemm_run_bsp.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Schedule), ctypes.c_int, vp]
     lib.agemm_run_pull.argtypes = [vp, vp, vp, vp, vp]
     lib.agemm_set_spin_timeout_us.argtypes = [vp, i64]
+    lib.agemm_timing_begin.argtypes = [vp, i32]
+    lib.agemm_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
     lib.agemm_check.argtypes = [vp]
     lib.agemm_last_error.argtypes = [vp]
     lib.agemm_last_error.restype = ctypes.c_char_p
@@ -176,6 +179,18 @@ class Context:
 
     def set_spin_timeout_us(self, us: int):
         self._raise(self._lib.agemm_set_spin_timeout_us(self._h, int(us)), "agemm_set_spin_timeout_us")
+
+    def timing_begin(self, max_launches: int):
+        """Time the next consumer kernel launches (events attached to their dispatch)."""
+        self._raise(self._lib.agemm_timing_begin(self._h, int(max_launches)), "agemm_timing_begin")
+
+    def timing_end(self):
+        """Synchronise on the timed launches; their kernel durations in microseconds."""
+        cap = 100000
+        buf = (ctypes.c_float * cap)()
+        n = ctypes.c_int32()
+        self._raise(self._lib.agemm_timing_end(self._h, buf, cap, ctypes.byref(n)), "agemm_timing_end")
+        return [float(buf[i]) for i in range(min(n.value, cap))]
 
     def check(self):
         """Raises AgemmError(ETIMEOUT) if a consumer timed out (call after synchronising)."""

@@ -13,6 +13,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "agemm_internal.h"
 
@@ -62,6 +63,12 @@ struct agemm_ctx {
   bool consumer_pending = false, producer_pending = false;
   bool fused_pending[2] = {false, false};
   bool consumed_this_epoch = false;
+
+  // Kernel timing (agemm_timing_begin/end): events attached to the dispatch
+  // of each consumer kernel launched while active, up to timing_cap launches.
+  std::vector<hipEvent_t> timing_events;  // start, stop pairs
+  int32_t timing_cap = 0, timing_count = 0;
+  bool timing_on = false;
 
   std::string last_error;
 };
@@ -156,6 +163,8 @@ int mark_consumer(agemm_ctx* c, hipStream_t s, hipEvent_t ev) {
   return AGEMM_OK;
 }
 
+LaunchTiming next_timing(agemm_ctx* c);
+
 // Launches the GEMM (a4-a6 of the path) with the given A source and gate.
 int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* B, void* C, hipStream_t s) {
   GemmArgs g{};
@@ -171,6 +180,7 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.tile_config = c->tile_config;
   g.gate = gate;
   const bool f32 = c->c_dtype == AGEMM_F32;
+  const LaunchTiming t = next_timing(c);
   hipError_t e;
   if (c->ws) {
     SmallMArgs sa{};
@@ -178,12 +188,23 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
     sa.plan = c->small_plan;
     sa.ws = c->ws;
     sa.counters = c->counters;
-    e = launch_gemm_small_m(sa, f32, s);
+    e = launch_gemm_small_m(sa, f32, s, t);
   } else {
-    e = launch_gemm_mfma(g, f32, s);
+    e = launch_gemm_mfma(g, f32, s, t);
   }
   if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
   return AGEMM_OK;
+}
+
+// The events for the next consumer launch (none when timing is off or full).
+LaunchTiming next_timing(agemm_ctx* c) {
+  LaunchTiming t;
+  if (c->timing_on && c->timing_count < c->timing_cap) {
+    t.start = c->timing_events[2 * c->timing_count];
+    t.stop = c->timing_events[2 * c->timing_count + 1];
+    c->timing_count++;
+  }
+  return t;
 }
 
 Gate no_gate(agemm_ctx* c) {
@@ -195,7 +216,15 @@ Gate no_gate(agemm_ctx* c) {
   return g;
 }
 
+void free_timing(agemm_ctx* c) {
+  for (hipEvent_t e : c->timing_events) hipEventDestroy(e);
+  c->timing_events.clear();
+  c->timing_cap = c->timing_count = 0;
+  c->timing_on = false;
+}
+
 void free_all(agemm_ctx* c) {
+  free_timing(c);
   if (c->inbox[0]) hipFree(c->inbox[0]);
   if (c->ctrl) hipFree(c->ctrl);
   if (c->gathered) hipFree(c->gathered);
@@ -484,6 +513,40 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
   return mark_consumer(ctx, s, ctx->ev_consumer);
+}
+
+int agemm_timing_begin(agemm_ctx* ctx, int32_t max_launches) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (max_launches < 1 || max_launches > 100000) return fail(ctx, AGEMM_EINVAL, "max_launches must be in 1..100000");
+  if (ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing already active");
+  if ((int32_t)ctx->timing_events.size() < 2 * max_launches) {
+    while ((int32_t)ctx->timing_events.size() < 2 * max_launches) {
+      hipEvent_t e = nullptr;
+      const hipError_t rc = hipEventCreate(&e);
+      if (rc != hipSuccess) return hip_fail(ctx, rc, "hipEventCreate");
+      ctx->timing_events.push_back(e);
+    }
+  }
+  ctx->timing_cap = max_launches;
+  ctx->timing_count = 0;
+  ctx->timing_on = true;
+  return AGEMM_OK;
+}
+
+int agemm_timing_end(agemm_ctx* ctx, float* us, int32_t max, int32_t* count) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (!ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing not active");
+  ctx->timing_on = false;
+  const int32_t n = ctx->timing_count;
+  if (count) *count = n;
+  for (int32_t i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(ctx->timing_events[2 * i + 1]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ctx->timing_events[2 * i], ctx->timing_events[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(ctx, e, "kernel timing events");
+    if (us && i < max) us[i] = ms * 1000.f;
+  }
+  return AGEMM_OK;
 }
 
 int agemm_check(agemm_ctx* ctx) {

@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,11 +85,18 @@ struct SmallMArgs {
   uint32_t* counters; // one per column block, zero between calls
 };
 
+// Optional HIP events attached to a consumer kernel's dispatch (its own start
+// and end timestamps); null = plain launch.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_produce(const ProduceArgs& a, hipStream_t s);
-hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 int mfma_config_count();
 int mfma_config_for(int64_t M, int tile_config);  // configuration launch_gemm_mfma uses
-hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s);
+hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 int small_m_limit();
 SmallMPlan small_m_plan(int W, int64_t M, int64_t KS, int64_t N, int num_cus);
 // The plan for given lanes / ranges / workgroups per CU, if the kernel takes it.

@@ -513,7 +513,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
 }
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN>
-hipError_t launch_cfg(const GemmArgs& a, bool out_f32, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   const int64_t MB = (a.M + BM - 1) / BM;
   const int64_t NB = (a.N + BN - 1) / BN;
   // Persistent grid of at most one workgroup per CU (the LDS ring admits no
@@ -523,7 +523,14 @@ hipError_t launch_cfg(const GemmArgs& a, bool out_f32, hipStream_t s) {
   const int64_t g = tiles < a.num_cus ? tiles : a.num_cus;
   const dim3 grid((unsigned)g), block(64 * WM * WN);
   const bool gated = a.gate.flags != nullptr;
-#define L(G_, F_) hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_>), grid, block, 0, s, a)
+#define L(G_, F_)                                                                                        \
+  do {                                                                                                  \
+    if (t.start)                                                                                        \
+      hipExtLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_>), grid, block, 0, s, t.start, \
+                            t.stop, 0, a);                                                              \
+    else                                                                                                \
+      hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_>), grid, block, 0, s, a);   \
+  } while (0)
   if (gated) { if (out_f32) L(true, true); else L(true, false); }
   else { if (out_f32) L(false, true); else L(false, false); }
 #undef L
@@ -539,12 +546,12 @@ int mfma_config_for(int64_t M, int tile_config) {
   return M > 192 ? 0 : 2;
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s) {
+hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   switch (mfma_config_for(a.M, a.tile_config)) {
-    case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, out_f32, s);   // 4 waves, 128x128 per wave
-    case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, out_f32, s);   // 8 waves, 128x64 per wave
-    case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, out_f32, s);   // 4 waves, 64x64 per wave
-    default: return launch_cfg<256, 256, 32, 4, 2, 4>(a, out_f32, s);  // 8 waves, 128x64, BK 32
+    case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, out_f32, s, t);   // 4 waves, 128x128 per wave
+    case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, out_f32, s, t);   // 8 waves, 128x64 per wave
+    case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, out_f32, s, t);   // 4 waves, 64x64 per wave
+    default: return launch_cfg<256, 256, 32, 4, 2, 4>(a, out_f32, s, t);  // 8 waves, 128x64, BK 32
   }
 }
 

@@ -296,23 +296,32 @@ size_t lds_bytes(int mt, int64_t rows_per_range, int lanes) {
   return sizeof(float) * ((size_t)mt * rows_per_range + (size_t)kWaves * 8 * lanes);
 }
 
+template <int MT, bool G, bool F>
+void launch_one(const SmallMArgs& a, dim3 grid, size_t lds, hipStream_t s, const LaunchTiming& t) {
+  if (t.start)
+    hipExtLaunchKernelGGL((gemm_small_m_kernel<MT, G, F>), grid, dim3(kThreads), (uint32_t)lds, s, t.start, t.stop, 0,
+                          a);
+  else
+    hipLaunchKernelGGL((gemm_small_m_kernel<MT, G, F>), grid, dim3(kThreads), lds, s, a);
+}
+
 template <int MT>
-hipError_t launch_mt(const SmallMArgs& a, bool out_f32, hipStream_t s) {
+hipError_t launch_mt(const SmallMArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   const SmallMPlan& p = a.plan;
-  // Persistent grid of at most kWgPerCu workgroups per CU (the plan makes the
-  // item count a multiple of that where it can): well under what fits on a
-  // CU, so producer workgroups always find room next to waiting consumers.
+  // Persistent grid of at most wg_per_cu workgroups per CU (the plan spreads
+  // the items evenly): well under what fits on a CU, so producer workgroups
+  // always find room next to waiting consumers.
   const int64_t items = (int64_t)p.ranges * p.nblk;
   const int64_t cap = (int64_t)p.wg_per_cu * a.g.num_cus;
   const dim3 grid((unsigned)(items < cap ? items : cap));
   const size_t lds = lds_bytes(MT, a.g.KS * (a.g.W / p.ranges), p.lanes);
   const bool gated = a.g.gate.flags != nullptr;
   if (gated) {
-    if (out_f32) hipLaunchKernelGGL((gemm_small_m_kernel<MT, true, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((gemm_small_m_kernel<MT, true, false>), grid, dim3(kThreads), lds, s, a);
+    if (out_f32) launch_one<MT, true, true>(a, grid, lds, s, t);
+    else launch_one<MT, true, false>(a, grid, lds, s, t);
   } else {
-    if (out_f32) hipLaunchKernelGGL((gemm_small_m_kernel<MT, false, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((gemm_small_m_kernel<MT, false, false>), grid, dim3(kThreads), lds, s, a);
+    if (out_f32) launch_one<MT, false, true>(a, grid, lds, s, t);
+    else launch_one<MT, false, false>(a, grid, lds, s, t);
   }
   return hipGetLastError();
 }
@@ -371,12 +380,12 @@ SmallMPlan small_m_plan_with(int W, int64_t M, int64_t KS, int64_t N, int lanes,
   return p;
 }
 
-hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s) {
+hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   const int64_t M = a.g.M;
-  if (M <= 1) return launch_mt<1>(a, out_f32, s);
-  if (M <= 2) return launch_mt<2>(a, out_f32, s);
-  if (M <= 4) return launch_mt<4>(a, out_f32, s);
-  return launch_mt<8>(a, out_f32, s);
+  if (M <= 1) return launch_mt<1>(a, out_f32, s, t);
+  if (M <= 2) return launch_mt<2>(a, out_f32, s, t);
+  if (M <= 4) return launch_mt<4>(a, out_f32, s, t);
+  return launch_mt<8>(a, out_f32, s, t);
 }
 
 }  // namespace agemm

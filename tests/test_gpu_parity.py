@@ -160,3 +160,28 @@ def test_every_tile_config(tile_config, W, M, K, N, monkeypatch):
         C = gu.empty_c(M, N, "f32")
         _run(ctx, path, dsh, B, C, schedule=(order, offs) if path != "pull" else None)
         assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), (tile_config, path)
+
+
+def test_kernel_timing_events():
+    """agemm_timing_begin/end: one duration per consumer launch (capped), in launch
+    order, positive; end without begin is a state error."""
+    import torch
+    from shard_decomposed_gemm_amd import AgemmError
+    from shard_decomposed_gemm_amd.agemm import ESTATE
+    W, M, K, N = 8, 130, 2048, 520
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=91)
+    ctx = _ctx(W, M, K, N, "f32")
+    C = gu.empty_c(M, N, "f32")
+    ctx.timing_begin(2)
+    for _ in range(3):
+        ctx.produce(dsh)
+        ctx.run_fused(B, C)
+    ctx.run_pull(dsh, B, C)
+    torch.cuda.synchronize()
+    us = ctx.timing_end()
+    assert len(us) == 2 and all(0.0 < u < 1e6 for u in us), us
+    with pytest.raises(AgemmError) as ei:
+        ctx.timing_end()
+    assert ei.value.status == ESTATE
+    ctx.check()
+    assert np.abs(gu.c_to_f64(C) - oracle.sharded_gemm(sh, b)).max() <= oracle.tolerance(K)
