@@ -173,26 +173,34 @@ def main():
         ctx.produce(shards, schedule=sched, stream=sp)
         ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc)
 
-    # ---- the timed fused steps: wall clock between two device synchronisations,
-    # and the consumer kernel's duration from HIP events attached to each of its
-    # dispatches on the consumer stream (agemm_timing_begin/end)
+    # ---- the timed fused steps (wall clock between two device synchronisations)
     for i in range(args.warmup):
         fused_step(i)
     torch.cuda.synchronize()
-    ctx.timing_begin(args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         fused_step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ctx.check()
+    # ---- the same steps again, with HIP events attached to each consumer dispatch on
+    # the consumer stream (agemm_timing_begin/end): the dominant kernel's own
+    # execution time. Attaching events costs a few microseconds per step between
+    # kernels, so the headline value comes from the pass above.
+    ctx.timing_begin(args.steps)
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        fused_step(i)
+    torch.cuda.synchronize()
+    wall_timed = time.perf_counter() - t1
     kern_us = ctx.timing_end()
     ctx.check()
     ms_step = wall * 1e3 / args.steps
     flops, cons_bytes, path_bytes = algorithmic(W, M, K, N, c_bytes)
     value = flops / (ms_step * 1e-3) / 1e12
     kavg = float(np.mean(kern_us)) * 1e-3  # ms
-    print(f"[bench] fused: {ms_step * 1e3:.1f} us/step, consumer kernel {kavg * 1e3:.1f} us avg "
-          f"({len(kern_us)} launches timed)", file=sys.stderr, flush=True)
+    print(f"[bench] fused: {ms_step * 1e3:.1f} us/step ({wall_timed * 1e6 / args.steps:.1f} with kernel timing), "
+          f"consumer kernel {kavg * 1e3:.1f} us avg over {len(kern_us)} launches", file=sys.stderr, flush=True)
 
     mfma_bound = flops / (PEAK_FP16_TFLOPS * 1e12) > cons_bytes / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
@@ -212,7 +220,8 @@ def main():
     roof["flops_per_launch"] = flops
     roof["kernel_us_avg"] = kavg * 1e3
     roof["kernel_us_min"] = float(np.min(kern_us))
-    roof["kernel_timing"] = "HIP events attached to each consumer dispatch in the timed loop"
+    roof["kernel_timing"] = ("HIP events attached to each consumer dispatch, over a second pass of the same "
+                             "timed steps")
 
     # ---- the BSP ladder on the same GPU
     ladder = None
@@ -256,6 +265,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_with_kernel_timing": wall_timed * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
