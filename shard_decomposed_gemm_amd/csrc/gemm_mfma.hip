@@ -4,11 +4,15 @@
 // Multi-GPU Performance Taxes" analysis page, AG+GEMM core identity): each
 // workgroup owns BM x BN tiles of C (persistent loop over tiles) and walks K
 // shard by shard, the loop order the page gives for the Pull and Push GEMMs.
-// With the gate on (Push model) each wave checks, before it issues the loads
-// of a k-step of (shard, k-tile), that the tile's flag has reached the
-// epoch's target: its lanes poll all T flags at once with relaxed agent-scope
-// loads, and the wave remembers which tiles it has seen raised, so a launch
-// that finds every flag raised pays for one poll per wave.
+// With the gate on (Push model) each wave checks, when its load cursor enters
+// a (shard, k-tile) and before any load of that tile, that the tile's flag
+// has reached the epoch's target: its lanes poll all T flags at once with
+// relaxed agent-scope loads, and the wave remembers which tiles it has seen
+// raised, so a launch that finds every flag raised pays for one poll per
+// wave. The check sits in the cursor's tile-crossing branch (taken once per
+// k-tile), not in the per-k-step path: a gate test in every k-step, or a
+// second gate-free copy of the loop beside a gated one, measurably slowed the
+// MFMA issue of the whole kernel.
 //
 // Data path (BK-wide k-steps, ring of STAGES LDS buffers):
 //   A_s, B -> LDS : 16-byte direct loads (global_load_lds). One uniform base
@@ -95,11 +99,6 @@ struct Shape {
   static_assert(KSUB == 2 || KSUB == 4, "two or four k-substeps");
   static_assert(LPS * KSUB == LOADS && LPS <= NMF, "loads must spread evenly over the substeps");
   static_assert(FM <= 4 && FN <= 4, "at most 4x4 MFMA blocks per wave");
-};
-
-template <bool B>
-struct Check {
-  static constexpr bool value = B;
 };
 
 template <int FM, int FN>
@@ -232,6 +231,55 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   uint32_t a_off[S::A_ITERS], b_off[S::B_ITERS];
   const int64_t lda2 = g.a.lda * 2;
 
+  // Flag gate of the tile the cursor enters (called from cursor_enter and at
+  // each flag-tile crossing of cursor_advance, before any load of the tile).
+  // `ready` (wave-uniform) remembers the tiles this wave has seen raised. A wave whose wait times out records the
+  // error and stops waiting; the launch still runs to its end with the same
+  // barrier sequence, and C is undefined.
+  uint64_t ready = 0;
+  bool dead = false;
+  auto gate = [&](const int tile) {
+    if constexpr (GATED) {
+      // Fast path (tile already seen, or given up) falls through without a
+      // taken branch: with one wave per SIMD a taken branch per k-step stalls
+      // the MFMA issue measurably.
+      if (__builtin_expect(((ready >> tile) & 1ull) || dead, 1)) return;
+      const uint64_t start = wall_clock();
+      uint64_t mask = 0;
+      uint32_t seen = 0;
+      while (true) {
+        bool up = false;
+        if (lane < g.gate.t) {
+          const uint32_t v = __hip_atomic_load(const_cast<uint32_t*>(g.gate.flags) + lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          up = (int32_t)(v - g.gate.target) >= 0;
+          if (lane == tile) seen = v;
+        }
+        mask = __ballot(up);
+        if ((mask >> tile) & 1ull) break;
+        if (wall_clock() - start > g.gate.timeout_ticks) {
+          dead = true;
+          if (lane == tile) {
+            __hip_atomic_store(&g.gate.err->tile, (uint32_t)tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&g.gate.err->target, g.gate.target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&g.gate.err->seen, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&g.gate.err->code, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      // The tiles' inbox lines have not been read in this launch before their
+      // flags were seen, so no cache holds a stale copy, and the loads that
+      // follow are ordered after the flag values by control dependency. The
+      // strict mode adds the formal agent-scope acquire (an L2-wide
+      // invalidate, costly when many waves issue it).
+      if (g.gate.strict) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      asm volatile("" ::: "memory");
+      ready = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32)) << 32) |
+              (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)mask);
+    }
+  };
   // Tile w -> (m0, n0). Workgroups are dealt round-robin to the 8 XCDs; each
   // XCD gets a contiguous range of logical tiles, ordered in groups of 8
   // row-blocks, so the tiles running together on one XCD share A and B rows
@@ -274,6 +322,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     ca = (const char*)g.a.base[0] + a_row0;
     cb = (const char*)g.B + n0 * 2;
     ct = 0; cs = 0; cts = 0; cft = 0; cfsub = 0;
+    gate(0);
   };
   auto cursor_advance = [&]() {
     if (++ct == NS) {
@@ -294,58 +343,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     } else {
       ca += BK * 2;
     }
-    if (++cfsub == spt) { cfsub = 0; ++cft; }
-  };
-
-  // Flag gate of the cursor's k-step. `ready` (wave-uniform) remembers the
-  // tiles this wave has seen raised. A wave whose wait times out records the
-  // error and stops waiting; the launch still runs to its end with the same
-  // barrier sequence, and C is undefined.
-  uint64_t ready = 0;
-  bool dead = false;
-  auto gate = [&]() {
-    if constexpr (GATED) {
-      const int tile = cft;
-      // Fast path (tile already seen, or given up) falls through without a
-      // taken branch: with one wave per SIMD a taken branch per k-step stalls
-      // the MFMA issue measurably.
-      if (__builtin_expect(((ready >> tile) & 1ull) || dead, 1)) return;
-      const uint64_t start = wall_clock();
-      uint64_t mask = 0;
-      uint32_t seen = 0;
-      while (true) {
-        bool up = false;
-        if (lane < g.gate.t) {
-          const uint32_t v = __hip_atomic_load(const_cast<uint32_t*>(g.gate.flags) + lane, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-          up = (int32_t)(v - g.gate.target) >= 0;
-          if (lane == tile) seen = v;
-        }
-        mask = __ballot(up);
-        if ((mask >> tile) & 1ull) break;
-        if (wall_clock() - start > g.gate.timeout_ticks) {
-          dead = true;
-          if (lane == tile) {
-            __hip_atomic_store(&g.gate.err->tile, (uint32_t)tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            __hip_atomic_store(&g.gate.err->target, g.gate.target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            __hip_atomic_store(&g.gate.err->seen, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            __hip_atomic_store(&g.gate.err->code, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-          }
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      // The tiles' inbox lines have not been read in this launch before their
-      // flags were seen, so no cache holds a stale copy, and the loads that
-      // follow are ordered after the flag values by control dependency. The
-      // strict mode adds the formal agent-scope acquire (an L2-wide
-      // invalidate, costly when many waves issue it).
-      if (g.gate.strict) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      asm volatile("" ::: "memory");
-      ready = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32)) << 32) |
-              (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)mask);
+    if (++cfsub == spt) {
+      cfsub = 0;
+      ++cft;
+      gate(cft);
     }
   };
+
   auto issue_one = [&](int j, int buf) {
     char* dst = smem + buf * S::STAGE;
     if (j < S::A_ITERS)
@@ -381,7 +385,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   cursor_enter(cw);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p) {
-    gate();
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) issue_one(j, p);
     cursor_advance();
@@ -389,18 +392,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   wait_vmcnt<(STAGES - 2) * LOADS>();
   barrier();
   int dbuf = STAGES - 1;  // buffer the current interval's direct loads go to
-  gate();
 #pragma unroll
   for (int j = 0; j < LPS; ++j) issue_one(j, dbuf);
 #pragma unroll
   for (int r = 0; r < NR; ++r) read_one_ks<BM, BN, BK, WM, WN>(0, r, lds0, ra_ks, rb, F0);
 
-  // Each wave has polled every flag once above. If all of this epoch's
-  // flags were already up it runs a copy of the loop with no gate code at
-  // all (the gate's slow path in the loop body costs a few percent of MFMA
-  // issue even when never taken); otherwise the gated copy. Both copies issue
-  // the same barriers, so the waves of one workgroup may take different ones.
-  auto main_loop = [&](auto check) {
+  auto main_loop = [&]() {
     int buf = 0;
     for (int w = blockIdx.x; w < total; w += G) {
       f32x16 acc[FM][FN];
@@ -442,7 +439,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
         wait_vmcnt<(STAGES - 2) * LOADS>();
         barrier();
         dbuf = buf;
-        if constexpr (decltype(check)::value) gate();
         const uint32_t nxt = lds0 + nbuf * S::STAGE;
   #pragma unroll
         for (int i = 0; i < NMF; ++i) {
@@ -502,13 +498,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       }
     }
   };
-  if constexpr (GATED) {
-    const uint64_t all = g.gate.t >= 64 ? ~0ull : ((1ull << g.gate.t) - 1ull);
-    if (ready == all) main_loop(Check<false>{});
-    else main_loop(Check<true>{});
-  } else {
-    main_loop(Check<false>{});
-  }
+  main_loop();
   __builtin_amdgcn_s_waitcnt(0);
 }
 
