@@ -48,6 +48,9 @@ def _load():
         lib.synth_fill_f16.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
         lib.synth_schedule.restype = ctypes.c_int
         lib.synth_schedule.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_fill_f32.restype = ctypes.c_int
+        lib.synth_fill_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_double, ctypes.c_double]
         _lib = lib
     return _lib
 
@@ -65,6 +68,24 @@ def fill_f16(seed: int, count: int, start: int = 0) -> np.ndarray:
     if count:
         _load().synth_fill_f16(seed, start, out.ctypes.data, out.size, _threads())
     return out
+
+
+def fill_f32(seed: int, count: int, lo: float = -1.0, hi: float = 1.0, start: int = 0) -> np.ndarray:
+    """binary32 values in [lo, hi) of elements start .. start+count-1 of stream ``seed``."""
+    out = np.empty(int(count), dtype=np.float32)
+    if count:
+        lib = _load()
+        lib.synth_fill_f32(seed, start, out.ctypes.data, out.size, float(lo), float(hi))
+    return out
+
+
+def fd_partials(seed: int, W: int, H: int, D: int, lse_lo: float = 8.0, lse_hi: float = 16.0):
+    """Per-rank Flash-Decode partials: W normalised partial outputs (H x D, uniform [-1, 1))
+    and W log-sum-exp vectors (H, uniform [lse_lo, lse_hi)), both binary32. Rank s draws
+    from streams seed + 2s (outputs) and seed + 2s + 1 (statistics)."""
+    o = [fill_f32(seed + 2 * s, H * D).reshape(H, D) for s in range(W)]
+    lse = [fill_f32(seed + 2 * s + 1, H, lse_lo, lse_hi) for s in range(W)]
+    return o, lse
 
 
 def matrix_f16(seed: int, rows: int, cols: int) -> np.ndarray:

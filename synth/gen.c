@@ -19,6 +19,11 @@
  *           j = ((splitmix64(seed XOR i) >> 32) * (i+1)) >> 32
  *   delays: d_p = floor(u_p * max_delay_ns / 2^24), u_p = splitmix64(seed XOR (2^32 + p)) >> 40
  *   offset: offset_ns[p] = d_0 + ... + d_p (cumulative), tile order[p] released at offset_ns[p]
+ *
+ * fp32 recipe (the per-rank partial outputs and log-sum-exp statistics fed to
+ * the Flash-Decode combine): x = lo + (hi - lo) * u * 2^-24 in binary64 with
+ * u = splitmix64(seed XOR i) >> 40, then rounded to binary32 (round to
+ * nearest even). With lo = -1, hi = 1 every value is exact in binary32.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -123,6 +128,15 @@ int synth_fill_f16(uint64_t seed, uint64_t start, uint16_t* out, size_t count, i
   for (int t = 0; t < nthreads; t++) {
     if ((size_t)t * per >= count) break;
     if (created[t]) pthread_join(th[t], NULL);
+  }
+  return 0;
+}
+
+/* Fills out[k] = binary32 value of element (start + k) of the stream `seed` in [lo, hi). */
+int synth_fill_f32(uint64_t seed, uint64_t start, float* out, size_t count, double lo, double hi) {
+  for (size_t k = 0; k < count; k++) {
+    uint64_t u = splitmix64(seed ^ (start + k)) >> 40;
+    out[k] = (float)(lo + (hi - lo) * ((double)u * (1.0 / 16777216.0))); /* 2^-24 */
   }
   return 0;
 }

@@ -84,3 +84,26 @@ def test_schedule_is_permutation_with_cumulative_delays():
     assert np.array_equal(order, o2) and np.array_equal(offs, f2)
     o0, f0 = synth.schedule(0x5005, 32, 0)
     assert (f0 == 0).all() and np.array_equal(o0, order)
+
+
+@pytest.mark.parametrize("lo,hi", [(-1.0, 1.0), (8.0, 16.0)])
+def test_fill_f32_recipe(lo, hi):
+    """fp32 stream: lo + (hi - lo) * u * 2^-24 in binary64, rounded to binary32 by numpy."""
+    seed, n, start = 0x7003, 1 << 16, 12345
+    got = synth.fill_f32(seed, n, lo, hi, start=start)
+    idx = np.arange(start, start + n, dtype=np.uint64)
+    u = _splitmix64_numpy(np.uint64(seed) ^ idx) >> np.uint64(40)
+    ref = (lo + (hi - lo) * (u.astype(np.float64) * 2.0 ** -24)).astype(np.float32)
+    assert np.array_equal(got, ref)
+    assert got.min() >= lo and got.max() < hi
+    if (lo, hi) == (-1.0, 1.0):
+        # every value is a multiple of 2^-23 in [-1, 1): exact in binary32
+        assert np.array_equal(got.astype(np.float64), lo + (hi - lo) * (u.astype(np.float64) * 2.0 ** -24))
+
+
+def test_fd_partials_streams():
+    o, lse = synth.fd_partials(0x7100, 3, 4, 8)
+    assert len(o) == 3 and len(lse) == 3
+    assert o[1].shape == (4, 8) and lse[2].shape == (4,)
+    assert np.array_equal(o[1].ravel(), synth.fill_f32(0x7102, 32))
+    assert np.array_equal(lse[2], synth.fill_f32(0x7105, 4, 8.0, 16.0))
