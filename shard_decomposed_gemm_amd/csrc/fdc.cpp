@@ -1,0 +1,383 @@
+// C-ABI of the flag-gated Flash-Decode combine (declared in include/fdcombine.h).
+//
+// Host side only: validation, the context (two inboxes and their flags, the
+// gather buffer, the error word), stream ordering between epochs, kernel
+// timing. Every step of the arithmetic runs in fd_combine.hip.
+#include "fdcombine.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "agemm_internal.h"
+
+using namespace agemm;
+
+struct fdc_ctx {
+  FdLayout L{};
+  int32_t t = 0;  // W * nht
+  agemm_dtype out_dtype = AGEMM_F16;
+  int device = 0;
+  double ticks_per_ns = 0.1;
+  uint64_t timeout_ticks = 0;
+
+  char* inbox[2] = {nullptr, nullptr};  // one allocation, W * nht blocks each
+  char* gathered = nullptr;             // baseline's gather buffer, same layout
+  uint32_t* ctrl = nullptr;             // flags[2][64] | t0 fused[2] | t0 bsp[2]
+  uint32_t* flags[2] = {nullptr, nullptr};
+  uint64_t* t0_fused = nullptr;
+  uint64_t* t0_bsp = nullptr;
+  ErrWord* err_host = nullptr;
+  ErrWord* err_dev = nullptr;
+
+  uint32_t epoch = 0;                 // produce calls so far; epoch e uses inbox e & 1
+  uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox
+  uint32_t parity_fused = 0, parity_bsp = 0;
+
+  hipEvent_t ev_producer = nullptr;
+  hipEvent_t ev_fused[2] = {nullptr, nullptr};
+  hipEvent_t ev_bsp = nullptr;
+  hipStream_t producer_stream = nullptr, fused_stream[2] = {nullptr, nullptr}, bsp_stream = nullptr;
+  bool producer_pending = false, fused_pending[2] = {false, false}, bsp_pending = false;
+
+  std::vector<hipEvent_t> timing_events;
+  int32_t timing_cap = 0, timing_count = 0;
+  bool timing_on = false;
+
+  std::string last_error;
+};
+
+namespace {
+
+const char* kNames[] = {"AGEMM_OK", "AGEMM_EINVAL", "AGEMM_ESHAPE", "AGEMM_ENOMEM",
+                        "AGEMM_EHIP", "AGEMM_ETIMEOUT", "AGEMM_ESTATE"};
+
+int fail(fdc_ctx* c, int code, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->last_error = std::string(kNames[code]) + ": " + buf;
+  }
+  return code;
+}
+
+int hip_fail(fdc_ctx* c, hipError_t e, const char* what) {
+  return fail(c, AGEMM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_parts(fdc_ctx* c, const void* const* o_parts, const void* const* lse_parts) {
+  if (!o_parts || !lse_parts) return fail(c, AGEMM_EINVAL, "o_parts and lse_parts must be non-NULL");
+  for (int s = 0; s < c->L.W; ++s)
+    if (!aligned16(o_parts[s]) || !aligned16(lse_parts[s]))
+      return fail(c, AGEMM_EINVAL, "partial %d: NULL or not 16-byte aligned", s);
+  return AGEMM_OK;
+}
+
+int fill_schedule(fdc_ctx* c, const agemm_schedule* sched, FdProduceArgs& pa) {
+  pa.has_delay = 0;
+  for (int p = 0; p < c->t; ++p) {
+    pa.order[p] = p;
+    pa.offset_ticks[p] = 0;
+  }
+  if (!sched) return AGEMM_OK;
+  if (sched->n != c->t || !sched->order || !sched->offset_ns)
+    return fail(c, AGEMM_EINVAL, "schedule must have n == T (%d) entries and non-NULL arrays", c->t);
+  bool seen[kMaxTiles] = {};
+  int64_t prev = 0;
+  for (int p = 0; p < c->t; ++p) {
+    const int32_t tile = sched->order[p];
+    if (tile < 0 || tile >= c->t || seen[tile]) return fail(c, AGEMM_EINVAL, "schedule order is not a permutation");
+    seen[tile] = true;
+    const int64_t off = sched->offset_ns[p];
+    if (off < 0 || off < prev) return fail(c, AGEMM_EINVAL, "schedule offsets must be non-negative and non-decreasing");
+    const double ticks = (double)off * c->ticks_per_ns;
+    if (ticks > 1.0e9) return fail(c, AGEMM_EINVAL, "schedule offset %lld ns is over 10 s", (long long)off);
+    prev = off;
+    pa.order[p] = tile;
+    pa.offset_ticks[p] = (uint32_t)(ticks + 0.5);
+    if (pa.offset_ticks[p]) pa.has_delay = 1;
+  }
+  return AGEMM_OK;
+}
+
+void base_args(fdc_ctx* c, const void* const* o_parts, const void* const* lse_parts, FdProduceArgs& pa) {
+  pa.L = c->L;
+  for (int s = 0; s < kMaxShards; ++s) {
+    pa.o_src[s] = s < c->L.W ? static_cast<const float*>(o_parts[s]) : nullptr;
+    pa.lse_src[s] = s < c->L.W ? static_cast<const float*>(lse_parts[s]) : nullptr;
+  }
+}
+
+LaunchTiming next_timing(fdc_ctx* c) {
+  LaunchTiming t;
+  if (c->timing_on && c->timing_count < c->timing_cap) {
+    t.start = c->timing_events[2 * c->timing_count];
+    t.stop = c->timing_events[2 * c->timing_count + 1];
+    c->timing_count++;
+  }
+  return t;
+}
+
+int launch_combine(fdc_ctx* c, const char* src, const uint32_t* flags, uint32_t target, void* O, hipStream_t s) {
+  FdCombineArgs a{};
+  a.L = c->L;
+  a.src = src;
+  a.O = O;
+  a.flags = flags;
+  a.target = target;
+  a.timeout_ticks = c->timeout_ticks;
+  a.err = c->err_dev;
+  const hipError_t e = launch_fd_combine(a, c->out_dtype == AGEMM_F32, s, next_timing(c));
+  if (e != hipSuccess) return hip_fail(c, e, "combine launch");
+  return AGEMM_OK;
+}
+
+void free_all(fdc_ctx* c) {
+  for (hipEvent_t e : c->timing_events) (void)hipEventDestroy(e);
+  c->timing_events.clear();
+  if (c->inbox[0]) (void)hipFree(c->inbox[0]);
+  if (c->gathered) (void)hipFree(c->gathered);
+  if (c->ctrl) (void)hipFree(c->ctrl);
+  if (c->err_host) (void)hipHostFree(c->err_host);
+  if (c->ev_producer) (void)hipEventDestroy(c->ev_producer);
+  if (c->ev_bsp) (void)hipEventDestroy(c->ev_bsp);
+  for (int i = 0; i < 2; ++i)
+    if (c->ev_fused[i]) (void)hipEventDestroy(c->ev_fused[i]);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dtype out_dtype) {
+  if (!out) return AGEMM_EINVAL;
+  *out = nullptr;
+  if (out_dtype != AGEMM_F16 && out_dtype != AGEMM_F32) return AGEMM_EINVAL;
+  const int HT = heads_per_tile;
+  if (W < 1 || W > kMaxShards || H < 1 || (D != 64 && D != 128 && D != 256)) return AGEMM_ESHAPE;
+  if (HT < 4 || HT > 32 || HT % 4 || H % HT) return AGEMM_ESHAPE;
+  const int nht = H / HT;
+  if ((int64_t)W * nht > kMaxTiles) return AGEMM_ESHAPE;
+
+  fdc_ctx* c = new (std::nothrow) fdc_ctx();
+  if (!c) return AGEMM_ENOMEM;
+  c->L.W = W;
+  c->L.H = H;
+  c->L.D = D;
+  c->L.HT = HT;
+  c->L.nht = nht;
+  c->L.blk = (int64_t)HT * D * 4 + 128;  // outputs, then the statistics in a line of their own
+  c->t = W * nht;
+  c->out_dtype = out_dtype;
+
+  hipError_t e = hipGetDevice(&c->device);
+  int wall_khz = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, c->device);
+  if (e != hipSuccess || wall_khz <= 0) {
+    delete c;
+    return AGEMM_EHIP;
+  }
+  c->ticks_per_ns = (double)wall_khz / 1.0e6;
+  c->timeout_ticks = (uint64_t)(2.0e9 * c->ticks_per_ns);  // 2 s
+
+  const size_t inbox_bytes = (size_t)c->t * (size_t)c->L.blk;
+  const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 4 * sizeof(uint64_t);
+  bool ok = hipMalloc(&c->inbox[0], 2 * inbox_bytes) == hipSuccess;
+  ok = ok && hipMalloc(&c->gathered, inbox_bytes) == hipSuccess;
+  ok = ok && hipMalloc(&c->ctrl, ctrl_bytes) == hipSuccess;
+  if (!ok) {
+    free_all(c);
+    delete c;
+    return AGEMM_ENOMEM;
+  }
+  c->inbox[1] = c->inbox[0] + inbox_bytes;
+  c->flags[0] = c->ctrl;
+  c->flags[1] = c->ctrl + kMaxTiles;
+  c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + 2 * kMaxTiles);
+  c->t0_bsp = c->t0_fused + 2;
+  void* hp = nullptr;
+  e = hipMemset(c->ctrl, 0, ctrl_bytes);
+  if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);
+  if (e == hipSuccess) {
+    c->err_host = static_cast<ErrWord*>(hp);
+    std::memset(c->err_host, 0, sizeof(ErrWord));
+    void* dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, hp, 0);
+    c->err_dev = static_cast<ErrWord*>(dp);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_bsp, hipEventDisableTiming);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_fused[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_all(c);
+    delete c;
+    return AGEMM_EHIP;
+  }
+  *out = c;
+  return AGEMM_OK;
+}
+
+int fdc_destroy(fdc_ctx* ctx) {
+  if (!ctx) return AGEMM_OK;
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  free_all(ctx);
+  delete ctx;
+  return AGEMM_OK;
+}
+
+int fdc_tiles(const fdc_ctx* ctx, int32_t* t) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (t) *t = ctx->t;
+  return AGEMM_OK;
+}
+
+int fdc_set_spin_timeout_us(fdc_ctx* ctx, int64_t us) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (us < 1) return fail(ctx, AGEMM_EINVAL, "timeout must be positive");
+  ctx->timeout_ticks = (uint64_t)((double)us * 1000.0 * ctx->ticks_per_ns);
+  return AGEMM_OK;
+}
+
+int fdc_produce(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse_parts, const agemm_schedule* sched,
+                void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  int rc = check_parts(ctx, o_parts, lse_parts);
+  if (rc) return rc;
+  FdProduceArgs pa{};
+  rc = fill_schedule(ctx, sched, pa);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The inbox of this epoch was last read by the fused combine two epochs ago.
+  const int slot = (int)((ctx->epoch + 1) & 1u);
+  hipError_t e = hipSuccess;
+  if (ctx->fused_pending[slot] && ctx->fused_stream[slot] != s) e = hipStreamWaitEvent(s, ctx->ev_fused[slot], 0);
+  if (e == hipSuccess && ctx->producer_pending && ctx->producer_stream != s)
+    e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
+  base_args(ctx, o_parts, lse_parts, pa);
+  pa.dst = ctx->inbox[slot];
+  pa.flags = ctx->flags[slot];
+  pa.t0 = ctx->t0_fused;
+  pa.parity = ctx->parity_fused & 1u;
+  e = launch_fd_produce(pa, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "producer launch");
+  if (pa.has_delay) ctx->parity_fused++;
+  e = hipEventRecord(ctx->ev_producer, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+  ctx->producer_pending = true;
+  ctx->producer_stream = s;
+  ctx->epoch++;
+  ctx->slot_epochs[slot]++;
+  return AGEMM_OK;
+}
+
+int fdc_run_fused(fdc_ctx* ctx, void* O, void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (!aligned16(O)) return fail(ctx, AGEMM_EINVAL, "O must be non-NULL and 16-byte aligned");
+  if (ctx->epoch == 0) return fail(ctx, AGEMM_ESTATE, "run_fused before any produce");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int slot = (int)(ctx->epoch & 1u);
+  // One increment per tile per epoch on this inbox (wraps with the counters).
+  int rc = launch_combine(ctx, ctx->inbox[slot], ctx->flags[slot], ctx->slot_epochs[slot], O, s);
+  if (rc) return rc;
+  const hipError_t e = hipEventRecord(ctx->ev_fused[slot], s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+  ctx->fused_pending[slot] = true;
+  ctx->fused_stream[slot] = s;
+  return AGEMM_OK;
+}
+
+int fdc_run_bsp(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse_parts, void* O,
+                const agemm_schedule* sched, int host_sync, void* stream) {
+  if (!ctx) return AGEMM_EINVAL;
+  int rc = check_parts(ctx, o_parts, lse_parts);
+  if (rc) return rc;
+  if (!aligned16(O)) return fail(ctx, AGEMM_EINVAL, "O must be non-NULL and 16-byte aligned");
+  FdProduceArgs pa{};
+  rc = fill_schedule(ctx, sched, pa);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The gather buffer is shared by baseline calls: wait for the last one's combine.
+  hipError_t e = hipSuccess;
+  if (ctx->bsp_pending && ctx->bsp_stream != s) e = hipStreamWaitEvent(s, ctx->ev_bsp, 0);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
+  // 1) all-gather stand-in: every partial into the gather buffer
+  base_args(ctx, o_parts, lse_parts, pa);
+  pa.dst = ctx->gathered;
+  pa.flags = nullptr;
+  pa.t0 = ctx->t0_bsp;
+  pa.parity = ctx->parity_bsp & 1u;
+  e = launch_fd_produce(pa, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "gather launch");
+  if (pa.has_delay) ctx->parity_bsp++;
+  // 2) the bulk-synchronous barrier
+  if (host_sync) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
+  }
+  // 3) the same combine with the flags off
+  rc = launch_combine(ctx, ctx->gathered, nullptr, 0, O, s);
+  if (rc) return rc;
+  e = hipEventRecord(ctx->ev_bsp, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+  ctx->bsp_pending = true;
+  ctx->bsp_stream = s;
+  return AGEMM_OK;
+}
+
+int fdc_timing_begin(fdc_ctx* ctx, int32_t max_launches) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (max_launches < 1 || max_launches > 100000) return fail(ctx, AGEMM_EINVAL, "max_launches must be in 1..100000");
+  if (ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing already active");
+  while ((int32_t)ctx->timing_events.size() < 2 * max_launches) {
+    hipEvent_t ev = nullptr;
+    const hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventCreate");
+    ctx->timing_events.push_back(ev);
+  }
+  ctx->timing_cap = max_launches;
+  ctx->timing_count = 0;
+  ctx->timing_on = true;
+  return AGEMM_OK;
+}
+
+int fdc_timing_end(fdc_ctx* ctx, float* us, int32_t max, int32_t* count) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (!ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing not active");
+  ctx->timing_on = false;
+  const int32_t n = ctx->timing_count;
+  if (count) *count = n;
+  for (int32_t i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(ctx->timing_events[2 * i + 1]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ctx->timing_events[2 * i], ctx->timing_events[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(ctx, e, "kernel timing events");
+    if (us && i < max) us[i] = ms * 1000.f;
+  }
+  return AGEMM_OK;
+}
+
+int fdc_check(fdc_ctx* ctx) {
+  if (!ctx) return AGEMM_EINVAL;
+  volatile ErrWord* w = ctx->err_host;
+  if (w->code == 0) return AGEMM_OK;
+  const unsigned tile = w->tile, target = w->target, seen = w->seen;
+  w->code = 0;
+  return fail(ctx, AGEMM_ETIMEOUT, "combine gave up waiting for tile %u (flag %u, target %u)", tile, seen, target);
+}
+
+const char* fdc_last_error(fdc_ctx* ctx) { return ctx ? ctx->last_error.c_str() : ""; }
+
+}  // extern "C"

@@ -12,9 +12,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "agemm.h")
 
 
-def _declared():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(agemm_[a-z_]+)\s*\(", text, re.M)))
+HEADER_FD = os.path.join(ROOT, "include", "fdcombine.h")
+
+
+def _declared(header=HEADER, prefix="agemm_"):
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(" + prefix + r"[a-z_]+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_documented_entry_points():
@@ -26,8 +29,36 @@ def test_header_declares_the_documented_entry_points():
 
 def test_library_exports_every_declared_symbol():
     lib = agemm.load()
-    for name in _declared():
+    for name in _declared() + _declared(HEADER_FD, "fdc_"):
         assert hasattr(lib, name), name
+
+
+def test_fd_header_matches_binding():
+    from shard_decomposed_gemm_amd import fdc
+    names = _declared(HEADER_FD, "fdc_")
+    for must in ("fdc_create", "fdc_produce", "fdc_run_fused", "fdc_run_bsp"):
+        assert must in names
+    assert sorted(fdc.EXPORTED) == names
+    fdc.load()  # every signature resolves
+
+
+@pytest.mark.parametrize("W,H,D,HT,code", [
+    (0, 96, 128, 16, agemm.ESHAPE),    # no ranks
+    (17, 96, 128, 16, agemm.ESHAPE),   # too many ranks
+    (8, 0, 128, 16, agemm.ESHAPE),     # no heads
+    (8, 96, 96, 16, agemm.ESHAPE),     # D not 64, 128 or 256
+    (8, 96, 128, 6, agemm.ESHAPE),     # heads per tile not a multiple of 4
+    (8, 96, 128, 36, agemm.ESHAPE),    # heads per tile above 32
+    (8, 100, 128, 16, agemm.ESHAPE),   # heads per tile does not divide H
+    (8, 96, 128, 4, agemm.ESHAPE),     # T = 8 * 24 = 192 tiles, above 64
+])
+def test_fd_create_rejects_bad_shapes_without_gpu(W, H, D, HT, code):
+    from shard_decomposed_gemm_amd import fdc
+    lib = fdc.load()
+    h = ctypes.c_void_p()
+    assert lib.fdc_create(ctypes.byref(h), W, H, D, HT, agemm.F16) == code
+    assert not h.value
+    assert lib.fdc_create(ctypes.byref(h), 8, 96, 128, 16, 7) == agemm.EINVAL  # unknown dtype
 
 
 def test_status_strings():
