@@ -35,13 +35,19 @@ WORKLOADS = {
     "prefill_m4096": (W_DEF, 4096, K_DEF, N_DEF, "f16", None),
     "ooo_m512": (W_DEF, 512, K_DEF, N_DEF, "f16", "random"),
 }
+# Flash-Decode combine (the pages' Flash-Decode shape: 96 query heads, d = 128, W = 8 ranks):
+# name: (W, H, D, heads per flag tile, output dtype, max delay between tile releases in ns)
+FD_WORKLOADS = {
+    "fd_combine_h96": (8, 96, 128, 16, "f16", 2_000),
+}
 # MI355X published peaks
 PEAK_FP16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
 CSRC = os.path.join(ROOT, "shard_decomposed_gemm_amd", "csrc")
-KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "agemm_internal.h"), "small_m": ("gemm_small_m.hip", "agemm_internal.h")}
+KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "agemm_internal.h"), "small_m": ("gemm_small_m.hip", "agemm_internal.h"),
+                  "fd": ("fd_combine.hip", "fd_internal.h", "agemm_internal.h")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "consumer_hbm_traffic.md")
 
 
@@ -104,6 +110,110 @@ def cpu_baseline(W, M, K, N, budget_s: float):
             "seconds": t1}
 
 
+def fd_cpu_baseline(W, H, D, budget_s: float):
+    """The combine oracle as it stands (numpy, binary64, one thread), called repeatedly
+    on the same partials for a bounded time."""
+    import synth
+    from oracle import fd as fdo
+    o, lse = synth.fd_partials(0x7A00, W, H, D)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fdo.combine(o, lse)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= 100000:
+            break
+    return {"value": dt / n * 1e6, "unit": "us per combine", "cores": 1, "kind": "oracle",
+            "sample": f"{n} combines of W={W} partials (H={H}, D={D}, binary64) in {dt:.2f} s", "seconds": dt}
+
+
+def run_fd(args):
+    """One step = producer of the W ranks' partial tiles (seeded release order and
+    delays) || flag-gated combine, on two streams."""
+    import numpy as np
+    import torch
+    import synth
+    from shard_decomposed_gemm_amd import FdCombine
+
+    W, H, D, HT, odt, max_delay = FD_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={args.workload} W={W} H={H} D={D} heads/tile={HT} out={odt}", file=sys.stderr, flush=True)
+    o, lse = synth.fd_partials(0x7A00, W, H, D)
+    do = [torch.from_numpy(x).to(dev) for x in o]
+    dl = [torch.from_numpy(x).to(dev) for x in lse]
+    Os = [torch.empty((H, D), dtype=torch.float16 if odt == "f16" else torch.float32, device=dev) for _ in range(2)]
+    ctx = FdCombine(W, H, D, heads_per_tile=HT, out_dtype=odt)
+    sched = synth.schedule(0x7A01, ctx.t, max_delay)
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step(i):
+        ctx.produce(do, dl, schedule=sched, stream=sp)
+        ctx.run_fused(Os[i & 1], stream=sc)
+
+    def timeit(fn, n):
+        for i in range(max(3, n // 5)):
+            fn(i)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e6 / n
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    us_step = (time.perf_counter() - t0) * 1e6 / args.steps
+    ctx.check()
+    ctx.timing_begin(args.steps)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = ctx.timing_end()
+    ctx.check()
+    kavg = float(np.mean(kern))
+    # algorithmic bytes of the combine kernel: every partial read once, the output written once
+    obytes = 2 if odt == "f16" else 4
+    cons_bytes = 4.0 * W * H * D + 4.0 * W * H + obytes * H * D
+    roof = {"bound": "hbm", "achieved": cons_bytes / (kavg * 1e-6) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": cons_bytes / (kavg * 1e-6) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+            "kernel": "flag-gated Flash-Decode combine (one wave per head)", "kernel_digest": kernel_digest("fd"),
+            "algorithmic_bytes_per_launch": cons_bytes, "kernel_us_avg": kavg, "kernel_us_min": float(np.min(kern)),
+            "note": "latency-bound: 0.4 MB per launch is far below what one launch takes to stream at HBM speed"}
+    ladder = None
+    if not args.no_ladder:
+        n = args.steps
+        bsp_sync = timeit(lambda i: ctx.run_bsp(do, dl, Os[i & 1], schedule=sched, host_sync=True, stream=sc), n)
+        bsp_dev = timeit(lambda i: ctx.run_bsp(do, dl, Os[i & 1], schedule=sched, host_sync=False, stream=sc), n)
+        fused = timeit(step, n)
+        ctx.produce(do, dl)
+        torch.cuda.synchronize()
+        alone = timeit(lambda i: ctx.run_fused(Os[i & 1], stream=sc), n)
+        ctx.check()
+        ladder = {"bsp_host_sync_us": bsp_sync, "bsp_device_dep_us": bsp_dev, "fused_us": fused,
+                  "consumer_only_us": alone, "fused_speedup_vs_bsp": bsp_sync / fused}
+        print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu else fd_cpu_baseline(W, H, D, min(args.cpu_budget, 10.0))
+    line = {
+        "metric": "Flash-Decode combine step latency (producer of W partials || flag-gated combine)",
+        "value": us_step, "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": us_step * 1e-3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "W": W, "H": H, "D": D, "heads_per_tile": HT, "out_dtype": odt,
+                   "tiles": ctx.t, "schedule": f"seeded permutation, cumulative U[0,{max_delay // 1000}] us delays",
+                   "release_span_us": float(sched[1][-1]) / 1e3},
+        "roofline": roof, "cpu_baseline": cpu, "ladder": ladder,
+    }
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
 def calibrate_copy(steps: int):
     """A plain device-to-device copy of 1 GiB: the known byte count (1 GiB read, 1 GiB
     written per dispatch) against which FETCH_SIZE / WRITE_SIZE are scaled."""
@@ -126,7 +236,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_m1", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="decode_m1", choices=list(WORKLOADS) + list(FD_WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
@@ -142,6 +252,9 @@ def main():
         print("bench.py measures one GPU: the flag-gated path keeps all W inbox slots in one GPU's HBM "
               "and this build has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in FD_WORKLOADS:
+        return run_fd(args)
 
     import numpy as np
     import torch

@@ -23,7 +23,7 @@
 // its own arrival order with no coordination; rounding depends on that order,
 // the exact value does not. Without flags (the baseline) the ranks go in
 // ascending order.
-#include "agemm_internal.h"
+#include "fd_internal.h"
 
 namespace agemm {
 namespace {

@@ -14,7 +14,7 @@
 #include <string>
 #include <vector>
 
-#include "agemm_internal.h"
+#include "fd_internal.h"
 
 using namespace agemm;
 
