@@ -6,6 +6,10 @@ flag-gated consumer GEMM runs on another (the Push model of the "Eliminating
 Multi-GPU Performance Taxes" analysis page). Inputs are seeded synthetic fp16
 uniform[-1, 1] and resident in HBM before timing starts.
 
+Before the counted warmup steps the step runs untimed for --prewarm-ms (default
+300 ms), so that the engine clock, which needs a few tens of milliseconds of
+continuous load to settle, is at its steady value when timing starts.
+
 Prints one JSON line. Besides the required fields it carries:
   roofline      the consumer kernel (the dominant one) against the fp16 MFMA
                 or HBM peak, timed with HIP events on the consumer's stream;
@@ -110,6 +114,21 @@ def cpu_baseline(W, M, K, N, budget_s: float):
             "seconds": t1}
 
 
+def prewarm(step, ms: float) -> int:
+    """Runs the step, untimed, for at least `ms` milliseconds of wall clock: the GPU's
+    engine clock takes a few tens of milliseconds of continuous load to reach its
+    steady value (measured: a register-only MFMA loop runs at 72 % of its steady rate
+    in its first 3 ms launch and needs about 20 back-to-back launches to settle)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def fd_cpu_baseline(W, H, D, budget_s: float):
     """The combine oracle as it stands (numpy, binary64, one thread), called repeatedly
     on the same partials for a bounded time."""
@@ -162,6 +181,7 @@ def run_fd(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t) * 1e6 / n
 
+    prewarm(step, args.prewarm_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -203,6 +223,7 @@ def run_fd(args):
     line = {
         "metric": "Flash-Decode combine step latency (producer of W partials || flag-gated combine)",
         "value": us_step, "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "prewarm_ms": args.prewarm_ms,
         "ms_per_step": us_step * 1e-3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "W": W, "H": H, "D": D, "heads_per_tile": HT, "out_dtype": odt,
@@ -238,6 +259,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_m1", choices=list(WORKLOADS) + list(FD_WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="untimed steps for this long before the warmup steps, so the engine clock has settled")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
@@ -287,6 +310,7 @@ def main():
         ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc)
 
     # ---- the timed fused steps (wall clock between two device synchronisations)
+    prewarm(fused_step, args.prewarm_ms)
     for i in range(args.warmup):
         fused_step(i)
     torch.cuda.synchronize()
@@ -377,6 +401,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_ms": args.prewarm_ms,
         "ms_per_step": ms_step,
         "ms_per_step_with_kernel_timing": wall_timed * 1e3 / args.steps,
         "higher_is_better": True,
