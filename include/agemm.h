@@ -14,8 +14,13 @@
  * K-slice at once instead of waiting for the whole all-gather. The page's
  * ordering requirement (its correctness check #4) is that a consumer which
  * sees the flag raised also sees the data. Here all W inbox slots live in the
- * HBM of one GPU and the ordering is an agent-scope release (producer) /
- * acquire (consumer) pair.
+ * HBM of one GPU. The producer writes a tile with device-coherent stores
+ * (written through to the coherence point), waits until they have completed,
+ * and only then increments the flag (relaxed, agent scope). The consumer
+ * polls the flags with relaxed agent-scope loads and reads no line of a tile
+ * before it has seen that tile's flag raised; its loads follow the flag value
+ * by control dependency. AGEMM_STRICT_ACQUIRE=1 in the environment at create
+ * time adds an agent-scope acquire fence after each wait.
  *
  * Layouts: every matrix is row-major fp16 (IEEE binary16) unless stated.
  *   A_s   M x KS, KS = K/W, row stride KS elements (one buffer per shard)
@@ -80,7 +85,14 @@ typedef struct {
 
 /* Creates a context for one shape. flag_ktile = BKf in elements; 0 picks
  * min(256, KS), widened until T <= 64. Allocates the inbox and the flags
- * (zeroed) on the current device. */
+ * (zeroed) on the current device. Tuning knobs read from the environment at
+ * this call (all optional; invalid values are ignored):
+ *   AGEMM_SPIN_TIMEOUT_MS    consumer flag-wait timeout (default 2000 ms)
+ *   AGEMM_STRICT_ACQUIRE=1   agent-scope acquire fence after each flag wait
+ *   AGEMM_TILE_CONFIG=0..3   MFMA tile configuration (default: from M)
+ *   AGEMM_SMALL_M_PLAN=l,r,w small-M work split: lanes, K-ranges, workgroups per CU
+ *   AGEMM_PRODUCER_ITEM_KIB  bytes of one tile copied by one producer workgroup
+ *                            (1..1024, default 16) */
 int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype,
                  int64_t flag_ktile);
 
