@@ -147,9 +147,9 @@ def test_call_order_and_argument_errors():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M", [1, 7, 300, 1024])
-def test_epoch_stress_bitwise(M, gate_mode):
-    """120 epochs cycle three data sets with jittered release schedules while the
+@pytest.mark.parametrize("M,epochs", [(1, 120), (7, 120), (300, 120), (1024, 120), (512, 1000)])
+def test_epoch_stress_bitwise(M, epochs, gate_mode):
+    """120 (at M = 512: 1000) epochs cycle three data sets with jittered release schedules while the
     consumer runs concurrently. Each epoch's C must equal, bit for bit, the ungated
     (pull) result of its own data set: a read of an inbox's previous content (another
     data set, since three sets cycle over two inboxes) would change it."""
@@ -168,7 +168,7 @@ def test_epoch_stress_bitwise(M, gate_mode):
     sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
     outs = [gu.empty_c(M, N, "f16") for _ in range(4)]
     bad = []
-    for e in range(120):
+    for e in range(epochs):
         p = probs[e % 3]
         order, offs = synth.schedule(0x5300 + e, ctx.t, (e % 5) * 3_000)
         C = outs[e % 4]
