@@ -217,7 +217,7 @@ Gate no_gate(agemm_ctx* c) {
 }
 
 void free_timing(agemm_ctx* c) {
-  for (hipEvent_t e : c->timing_events) hipEventDestroy(e);
+  for (hipEvent_t e : c->timing_events) (void)hipEventDestroy(e);
   c->timing_events.clear();
   c->timing_cap = c->timing_count = 0;
   c->timing_on = false;
@@ -225,16 +225,16 @@ void free_timing(agemm_ctx* c) {
 
 void free_all(agemm_ctx* c) {
   free_timing(c);
-  if (c->inbox[0]) hipFree(c->inbox[0]);
-  if (c->ctrl) hipFree(c->ctrl);
-  if (c->gathered) hipFree(c->gathered);
-  if (c->ws) hipFree(c->ws);
-  if (c->counters) hipFree(c->counters);
-  if (c->err_host) hipHostFree(c->err_host);
-  if (c->ev_consumer) hipEventDestroy(c->ev_consumer);
-  if (c->ev_producer) hipEventDestroy(c->ev_producer);
+  if (c->inbox[0]) (void)hipFree(c->inbox[0]);
+  if (c->ctrl) (void)hipFree(c->ctrl);
+  if (c->gathered) (void)hipFree(c->gathered);
+  if (c->ws) (void)hipFree(c->ws);
+  if (c->counters) (void)hipFree(c->counters);
+  if (c->err_host) (void)hipHostFree(c->err_host);
+  if (c->ev_consumer) (void)hipEventDestroy(c->ev_consumer);
+  if (c->ev_producer) (void)hipEventDestroy(c->ev_producer);
   for (int i = 0; i < 2; ++i)
-    if (c->ev_fused[i]) hipEventDestroy(c->ev_fused[i]);
+    if (c->ev_fused[i]) (void)hipEventDestroy(c->ev_fused[i]);
 }
 
 }  // namespace
@@ -378,8 +378,8 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
 
 int agemm_destroy(agemm_ctx* ctx) {
   if (!ctx) return AGEMM_OK;
-  hipSetDevice(ctx->device);
-  hipDeviceSynchronize();
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();  // a destroy cannot fail: release what was allocated
   free_all(ctx);
   delete ctx;
   return AGEMM_OK;

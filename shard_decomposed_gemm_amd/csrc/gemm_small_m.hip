@@ -42,7 +42,6 @@ constexpr size_t kLdsLimit = 64 * 1024;
 constexpr int kWgPerCu = 2;  // concurrent workgroups per CU: 8 waves keep enough B in flight
 
 __device__ inline uint64_t wall_clock() { return __builtin_amdgcn_s_memrealtime(); }
-__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Device-coherent (agent-scope) fp32 store and load of the split-K partials.
 __device__ inline void store_coherent(float* p, float v) {
