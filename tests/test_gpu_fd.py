@@ -98,6 +98,27 @@ def test_fd_exact_inputs_bitwise(path):
     assert np.array_equal(O.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("path", ["fused", "bsp"])
+def test_fd_against_stored_golden(path):
+    """W=4, H=16, d=64 against the binary64 O stored in tests/golden/ (written from
+    the oracle by tests/golden/make_golden.py)."""
+    import torch
+    from tests import golden_io
+    W, H, D, HT = 4, 16, 64, 8
+    o, lse = synth.fd_partials(0x7A00, W, H, D)
+    do, dl = _dev_parts(o, lse)
+    ctx = _ctx(W, H, D, HT, "f32")
+    O = _out(H, D, "f32")
+    if path == "fused":
+        _fused(ctx, do, dl, O)
+    else:
+        ctx.run_bsp(do, dl, O)
+        torch.cuda.synchronize()
+        ctx.check()
+    got = O.cpu().numpy().astype(np.float64)
+    assert np.abs(got - golden_io.fd()).max() <= fdo.tolerance("f32")
+
+
 def test_fd_poisoned_inbox_is_never_read_early():
     """Both inboxes hold NaN partials from two earlier epochs; the real epoch releases
     its tiles out of order, up to 40 us apart, while the combine already runs."""

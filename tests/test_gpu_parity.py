@@ -54,6 +54,21 @@ def test_tiny_config_flags_preset():
     assert err <= oracle.tolerance(K), err
 
 
+@pytest.mark.parametrize("path", ["fused", "fused_preset", "bsp", "pull"])
+@pytest.mark.parametrize("c_dtype", ["f32", "f16"])
+def test_tiny_config_against_stored_golden(path, c_dtype):
+    """The tiny workload against the exact C stored in tests/golden/ (written from the
+    oracle by tests/golden/make_golden.py), not against a live oracle call."""
+    from tests import golden_io
+    W, M, K, N = 8, 8, 512, 256
+    _, _, _, dsh, B = gu.random_problem(W, M, K, N, seed=1)
+    ctx = _ctx(W, M, K, N, c_dtype)
+    C = gu.empty_c(M, N, c_dtype)
+    _run(ctx, path, dsh, B, C)
+    err = np.abs(gu.c_to_f64(C) - golden_io.tiny_c()).max()
+    assert err <= oracle.tolerance(K), err
+
+
 SHAPES = [
     # W, M, K, N                      kernel exercised
     (8, 8, 512, 256),                 # small-M, tiny workload
