@@ -50,6 +50,39 @@ def test_poisoned_inbox_is_never_read_early(W, M, K, N, gate_mode):
     assert np.abs(got - ref).max() <= oracle.tolerance(K)
 
 
+@pytest.mark.parametrize("W,M,K,N,bkf", [
+    (8, 300, 8192, 1000, 128),   # 256x256 MFMA tiles, 8 flag tiles per shard
+    (8, 130, 4096, 520, 64),     # 128x128 MFMA tiles, one k-step per flag tile
+    (8, 4, 4096, 1032, 64),      # small-M streaming kernel
+    (8, 1, 4096, 1024, 64),      # small-M, M = 1
+    (16, 257, 16384, 264, 256),  # 16 shards of 4 flag tiles
+])
+def test_sixty_four_flags_out_of_order(W, M, K, N, bkf):
+    """The largest flag count, T = W * KS / BK_f = 64 (one flag per lane of the polling
+    wave), with a non-default flag k-tile: poisoned inboxes, then the 64 tiles released
+    in a seeded order with cumulative delays while the consumer runs."""
+    import torch
+    from shard_decomposed_gemm_amd import Context
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=43)
+    ref = oracle.sharded_gemm(sh, b)
+    ctx = Context(W, M, K, N, c_dtype="f32", flag_ktile=bkf)
+    assert ctx.t == 64
+    nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
+    ctx.produce(nan)
+    ctx.produce(nan)
+    torch.cuda.synchronize()
+    order, offs = synth.schedule(0x5300 + M, ctx.t, 10_000)
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    C = gu.empty_c(M, N, "f32")
+    ctx.produce(dsh, schedule=(order, offs), stream=sp)
+    ctx.run_fused(B, C, stream=sc)
+    torch.cuda.synchronize()
+    ctx.check()
+    got = gu.c_to_f64(C)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= oracle.tolerance(K)
+
+
 @pytest.mark.parametrize("M", [1, 256])
 def test_alternating_epochs(M, gate_mode):
     """Three data sets cycle over successive epochs on two streams (so each of the two
