@@ -352,8 +352,9 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None}
     kind, tile_cfg = ctx.consumer
     roof["traffic"] = measured_traffic(args.workload, kind)
-    roof["kernel"] = ("flag-gated MFMA tile GEMM, tile config %d" % tile_cfg if kind == "mfma"
-                      else "flag-gated small-M split-K streaming GEMM")
+    roof["kernel"] = ("flag-gated MFMA tile GEMM, tile config %d, %d workgroups%s"
+                      % (tile_cfg, ctx.grid, ", stream-K split over (tile, shard) units" if ctx.split else "")
+                      if kind == "mfma" else "flag-gated small-M split-K streaming GEMM")
     roof["kernel_digest"] = kernel_digest(kind)
     roof["algorithmic_bytes_per_launch"] = cons_bytes
     roof["flops_per_launch"] = flops

@@ -46,8 +46,20 @@
  *
  * Ownership: the context owns two inboxes (each W x M x KS fp16, used by
  * alternate epochs) with their flags (T uint32 counters each), the
- * gathered-A buffer of the BSP path, the split-K workspace and the error
- * word. The caller owns A_s, B, C and all streams.
+ * gathered-A buffer of the BSP path, the split-K workspaces and the error
+ * word. The caller owns A_s, B, C and all streams. Everything is allocated
+ * at create time; no other call allocates.
+ *
+ * Work split of the GEMM (fixed at create time). With few output tiles (at
+ * most half as many as the GPU's compute units) whole tiles would leave most
+ * units idle; the GEMM then deals equal runs of (output tile, shard) units to
+ * one workgroup per compute unit (stream-K). A tile whose shards
+ * fall to several workgroups is summed by the last of them to finish, in a
+ * fixed order (contributors' shard ranges ascending), from fp32 partials the
+ * others leave in the context's workspace; the result does not depend on
+ * timing, and the fused, BSP and pull paths of one context give identical C.
+ * Consumer calls of one context are ordered after each other (device side)
+ * because they share this workspace.
  * A context is not thread-safe; use one per host thread.
  */
 #ifndef AGEMM_H
@@ -90,6 +102,9 @@ typedef struct {
  *   AGEMM_SPIN_TIMEOUT_MS    consumer flag-wait timeout (default 2000 ms)
  *   AGEMM_STRICT_ACQUIRE=1   agent-scope acquire fence after each flag wait
  *   AGEMM_TILE_CONFIG=0..3   MFMA tile configuration (default: from M)
+ *   AGEMM_SPLIT=0|1          MFMA work split: 0 whole tiles only, 1 the stream-K
+ *                            split whenever W >= 2 (default: the split when whole
+ *                            tiles would leave at least half of the CUs idle)
  *   AGEMM_SMALL_M_PLAN=l,r,w small-M work split: lanes, K-ranges, workgroups per CU
  *   AGEMM_PRODUCER_ITEM_KIB  bytes of one tile copied by one producer workgroup
  *                            (1..1024, default 16) */
@@ -107,6 +122,11 @@ int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
  * small-M split-K streaming kernel (M <= 8; *tile_config = -1). Either output
  * pointer may be NULL. */
 int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_config);
+
+/* Launch shape of the MFMA consumer: *grid = its workgroups, *split = 1 when
+ * it runs the stream-K split described above, else 0. For the small-M kernel
+ * *grid = -1 and *split = 0. Either output pointer may be NULL. */
+int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split);
 
 /* Producer (Push model): copies tile (s, kt) of A_s into Inbox(s) and then
  * raises Flags(s, kt), for every tile, in the schedule's order and at its

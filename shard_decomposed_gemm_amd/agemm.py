@@ -19,7 +19,7 @@ OK, EINVAL, ESHAPE, ENOMEM, EHIP, ETIMEOUT, ESTATE = range(7)
 F16, F32 = 0, 1
 
 EXPORTED = (
-    "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_produce", "agemm_run_fused",
+    "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_produce", "agemm_run_fused",
     "agemm_run_bsp", "agemm_run_pull", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
     "agemm_check",
     "agemm_last_error", "agemm_status_string",
@@ -52,6 +52,7 @@ def load() -> ctypes.CDLL:
     lib.agemm_destroy.argtypes = [vp]
     lib.agemm_tiles.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_consumer_kernel.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.agemm_consumer_grid.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_produce.argtypes = [vp, vp, ctypes.POINTER(Schedule), vp]
     lib.agemm_run_fused.argtypes = [vp, vp, vp, vp]
     lib.agemm_run_bsp.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Schedule), ctypes.c_int, vp]
@@ -127,6 +128,10 @@ class Context:
         lib.agemm_consumer_kernel(h, ctypes.byref(kind), ctypes.byref(cfg))
         # consumer kernel of this context: ("mfma", tile config) or ("small_m", -1)
         self.consumer = ("small_m" if kind.value == 1 else "mfma", cfg.value)
+        grid, split = ctypes.c_int32(), ctypes.c_int32()
+        lib.agemm_consumer_grid(h, ctypes.byref(grid), ctypes.byref(split))
+        # MFMA consumer's workgroups (-1 for small-M) and whether it runs the stream-K split
+        self.grid, self.split = grid.value, bool(split.value)
 
     # -- helpers
     def _raise(self, rc: int, what: str):

@@ -43,6 +43,9 @@ struct agemm_ctx {
   SmallMPlan small_plan;         // small-M work split (small_plan.ok: the small-M kernel is used)
   float* ws = nullptr;           // small-M split-K workspace, ranges x M x N
   uint32_t* counters = nullptr;  // small-M column-block counters
+  MfmaPlan mplan;                // MFMA consumer plan (when the small-M kernel is not used)
+  float* mws = nullptr;          // MFMA stream-K partial slots (mplan.split)
+  uint32_t* mcnt = nullptr;      // MFMA stream-K tile counters (mplan.split)
   ErrWord* err_host = nullptr;
   ErrWord* err_dev = nullptr;
 
@@ -179,6 +182,9 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.num_cus = c->num_cus;
   g.tile_config = c->tile_config;
   g.gate = gate;
+  g.split = c->mplan.split ? 1 : 0;
+  g.split_ws = c->mws;
+  g.split_cnt = c->mcnt;
   const bool f32 = c->c_dtype == AGEMM_F32;
   const LaunchTiming t = next_timing(c);
   hipError_t e;
@@ -230,6 +236,8 @@ void free_all(agemm_ctx* c) {
   if (c->gathered) (void)hipFree(c->gathered);
   if (c->ws) (void)hipFree(c->ws);
   if (c->counters) (void)hipFree(c->counters);
+  if (c->mws) (void)hipFree(c->mws);
+  if (c->mcnt) (void)hipFree(c->mcnt);
   if (c->err_host) (void)hipHostFree(c->err_host);
   if (c->ev_consumer) (void)hipEventDestroy(c->ev_consumer);
   if (c->ev_producer) (void)hipEventDestroy(c->ev_producer);
@@ -333,6 +341,11 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     }
   }
   const bool small = c->small_plan.ok;
+  if (!small) {
+    int split_mode = -1;
+    if (const char* env = std::getenv("AGEMM_SPLIT")) split_mode = std::atoi(env) != 0 ? 1 : 0;
+    c->mplan = mfma_plan(M, N, W, c->num_cus, c->tile_config, split_mode);
+  }
   const size_t ws_bytes = small ? sizeof(float) * (size_t)c->small_plan.ranges * (size_t)M * (size_t)N : 0;
   const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)c->small_plan.nblk : 0;
   bool ok = hipMalloc(&c->inbox[0], 2 * inbox_bytes) == hipSuccess;
@@ -342,6 +355,11 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     ok = hipMalloc(&c->ws, ws_bytes) == hipSuccess;
     ok = ok && hipMalloc(&c->counters, cnt_bytes) == hipSuccess;
     ok = ok && hipMemset(c->counters, 0, cnt_bytes) == hipSuccess;
+  }
+  if (ok && c->mplan.split) {
+    ok = hipMalloc(&c->mws, c->mplan.ws_bytes) == hipSuccess;
+    ok = ok && hipMalloc(&c->mcnt, c->mplan.cnt_bytes) == hipSuccess;
+    ok = ok && hipMemset(c->mcnt, 0, c->mplan.cnt_bytes) == hipSuccess;
   }
   if (!ok) {
     free_all(c);
@@ -398,6 +416,14 @@ int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_con
   const bool small = ctx->ws != nullptr;
   if (kind) *kind = small ? 1 : 0;
   if (tile_config) *tile_config = small ? -1 : mfma_config_for(ctx->M, ctx->tile_config);
+  return AGEMM_OK;
+}
+
+int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split) {
+  if (!ctx) return AGEMM_EINVAL;
+  const bool small = ctx->ws != nullptr;
+  if (grid) *grid = small ? -1 : (int32_t)ctx->mplan.grid;
+  if (split) *split = small ? 0 : (ctx->mplan.split ? 1 : 0);
   return AGEMM_OK;
 }
 
@@ -564,12 +590,12 @@ int agemm_check(agemm_ctx* ctx) {
   if (w->code == 0) return AGEMM_OK;
   const unsigned tile = w->tile, target = w->target, seen = w->seen;
   w->code = 0;
-  // A timed-out small-M launch leaves its column counters part-way; clear them.
-  if (ctx->counters) {
-    hipError_t e = hipMemset(ctx->counters, 0, sizeof(uint32_t) * (size_t)ctx->small_plan.nblk);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemset(counters)");
-  }
+  // A timed-out launch can leave split-K counters part-way; clear them.
+  hipError_t e = hipSuccess;
+  if (ctx->counters) e = hipMemset(ctx->counters, 0, sizeof(uint32_t) * (size_t)ctx->small_plan.nblk);
+  if (e == hipSuccess && ctx->mcnt) e = hipMemset(ctx->mcnt, 0, ctx->mplan.cnt_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipMemset(counters)");
   return fail(ctx, AGEMM_ETIMEOUT, "consumer gave up waiting for tile %u (flag %u, target %u)", tile, seen, target);
 }
 

@@ -44,6 +44,25 @@ struct GemmArgs {
   int32_t num_cus;    // compute units of the device (persistent grid size)
   int32_t tile_config;  // MFMA tile configuration, -1 = chosen from the shape
   Gate gate;
+  // Stream-K split of the MFMA consumer (split != 0): the grid's workgroups
+  // take equal runs of (output tile, shard) units in tile-major order; a tile
+  // whose units fall to several workgroups is summed by the last of them to
+  // finish, in contributor order, from partials the others publish.
+  int32_t split;
+  float* split_ws;      // 2 * grid slots of BM x BN fp32 partials
+  uint32_t* split_cnt;  // one ticket counter per output tile, zero between calls
+};
+
+// Launch plan of the MFMA consumer for a shape, fixed when a context is
+// created: tile configuration, grid, and whether the stream-K split is used.
+struct MfmaPlan {
+  int cfg = 0;
+  int64_t bm = 0, bn = 0;
+  int64_t tiles = 0;     // output tiles
+  int64_t grid = 0;      // workgroups of the persistent grid
+  bool split = false;
+  size_t ws_bytes = 0;   // split partial slots
+  size_t cnt_bytes = 0;  // split counters
 };
 
 // Producer: copies item (position p in release order, row chunk q) from A_s to
@@ -96,6 +115,8 @@ hipError_t launch_produce(const ProduceArgs& a, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 int mfma_config_count();
 int mfma_config_for(int64_t M, int tile_config);  // configuration launch_gemm_mfma uses
+// split_mode: -1 = split when it shortens the busiest workgroup's run, 0 = never, 1 = whenever W >= 2.
+MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode);
 hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 int small_m_limit();
 SmallMPlan small_m_plan(int W, int64_t M, int64_t KS, int64_t N, int num_cus);

@@ -45,6 +45,8 @@
 // direct-load waits, the per-k-step barrier).
 #include "agemm_internal.h"
 
+#include <algorithm>
+
 namespace agemm {
 namespace {
 
@@ -54,6 +56,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 __device__ inline uint64_t wall_clock() { return __builtin_amdgcn_s_memrealtime(); }
+// A 64-lane ballot made wave-uniform. readfirstlane returns a signed int:
+// each half goes through uint32_t so that bit 31 is not sign-extended into
+// the upper half (which would mark every flag tile from 32 on as raised).
+__device__ inline uint64_t uniform_mask(uint64_t mask) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)mask);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(mask >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
 __device__ inline int swz_b(int k) { return (k & 3) << 2; }
 template <int CPR>
 __device__ inline int swz_a(int row) { return (row / (16 / CPR)) % CPR; }
@@ -168,7 +178,17 @@ __device__ __attribute__((always_inline)) inline void mfma_one(const Frags<FM, F
     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, f.a[fm], acc[fm][fn], 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool GATED, bool OUTF32>
+// Device-coherent (agent-scope) 8-byte store and load of the split-K partials:
+// they bypass the per-XCD L2s, so a partial written on one XCD is read
+// correctly on another without an L2-wide fence.
+__device__ inline void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool GATED, bool OUTF32, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   using S = Shape<BM, BN, BK, WM, WN>;
   constexpr int NT = S::NT, TM = S::TM, TN = S::TN, FM = S::FM, FN = S::FN, LOADS = S::LOADS;
@@ -197,6 +217,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   const int G = gridDim.x;
   const bool xcd_split = (total % 8 == 0) && (G % 8 == 0);
 
+  // Work of this workgroup as segments: a tile and its k-steps [kb, ke).
+  // Without the split, tiles blockIdx.x, blockIdx.x + G, ... in full. With
+  // it, the units [u0, u1) of the workgroup's run (unit = (tile, shard),
+  // tile-major; the run of workgroup b is [floor(b*U/G), floor((b+1)*U/G))),
+  // cut at tile borders, so only the first and last segments can be partial.
+  // Runs are numbered so that consecutive runs share an XCD (workgroups are
+  // dealt round-robin to the 8 XCDs) and work on neighbouring tiles.
+  const int Wsh = g.W;
+  const int64_t U = (int64_t)total * Wsh;
+  const int bp = (SPLIT && G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int64_t u0 = (int64_t)bp * U / G, u1 = (int64_t)(bp + 1) * U / G;
+  struct Seg {
+    int w, kb, ke;
+  };
+  auto seg_end = [&](int w) {
+    const int64_t e = u1 < (int64_t)(w + 1) * Wsh ? u1 : (int64_t)(w + 1) * Wsh;
+    return (int)(e - (int64_t)w * Wsh) * SPS;
+  };
+  auto seg_first = [&](Seg& q) {
+    if constexpr (SPLIT) {
+      q.w = (int)(u0 / Wsh);
+      q.kb = (int)(u0 - (int64_t)q.w * Wsh) * SPS;
+      q.ke = seg_end(q.w);
+    } else {
+      q.w = blockIdx.x;
+      q.kb = 0;
+      q.ke = NS;
+    }
+  };
+  // Advances q to the next segment; false (q unchanged) when there is none.
+  auto seg_next = [&](Seg& q) -> bool {
+    if constexpr (SPLIT) {
+      const int w = q.w + 1;
+      if ((int64_t)w * Wsh >= u1) return false;
+      q.w = w;
+      q.kb = 0;
+      q.ke = seg_end(w);
+    } else {
+      const int w = q.w + G;
+      if (w >= total) return false;
+      q.w = w;
+    }
+    return true;
+  };
+
   // LDS read offsets, fixed for the launch. B (transpose read, 16-lane
   // groups): lane supplies row k = 16*ks + 8*(g/2) + 4*h + (i/4) and columns
   // n = fn*32 + 16*(g%2) + 4*(i%4) of the wave's range, stored at chunk
@@ -224,7 +289,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   // advanced with additions only; its flag tile feeds the gate. Past the last
   // tile it keeps re-loading the last step into buffers nobody reads, which
   // keeps the count of loads in flight, and so every wait, uniform.
-  int cw = blockIdx.x;                       // tile (persistent-loop index)
+  Seg cseg;                                  // segment of the cursor
+  seg_first(cseg);
   int ct = 0, cs = 0, cts = 0;               // k-step in the tile, shard, k-step in the shard
   int cft = 0, cfsub = 0;                    // flag tile, k-step within it
   const int spt = SPS / g.gate.kt;
@@ -279,16 +345,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       // invalidate, costly when many waves issue it).
       if (g.gate.strict) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       asm volatile("" ::: "memory");
-      ready = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32)) << 32) |
-              (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)mask);
+      ready = uniform_mask(mask);
     }
   };
   // Tile w -> (m0, n0). Workgroups are dealt round-robin to the 8 XCDs; each
   // XCD gets a contiguous range of logical tiles, ordered in groups of 8
   // row-blocks, so the tiles running together on one XCD share A and B rows
   // in its L2.
+  // (With the split, w is already a logical index: the runs are numbered by XCD.)
   auto tile_coords = [&](int w, int64_t& m0, int64_t& n0) {
-    const int logical = xcd_split ? (w % 8) * (total / 8) + (w / 8) : w;
+    const int logical = (!SPLIT && xcd_split) ? (w % 8) * (total / 8) + (w / 8) : w;
     constexpr int GM = 8;
     const int group = logical / (GM * NB);
     const int first_m = group * GM;
@@ -300,9 +366,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   // Lane offsets of tile w: the LDS destination of chunk q is byte q*16 of
   // the stage; rows past M and columns past N re-load a valid row/column
   // whose results are never stored. m0 and n0 go into the base pointers.
-  auto cursor_enter = [&](int w) {
+  auto cursor_enter = [&]() {
     int64_t m0, n0;
-    tile_coords(w, m0, n0);
+    tile_coords(cseg.w, m0, n0);
     const int rmax = (int)(M - 1 - m0);
 #pragma unroll
     for (int j = 0; j < S::A_ITERS; ++j) {
@@ -322,20 +388,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       b_off[j] = (uint32_t)((k * N + c) * 2);
     }
     a_row0 = m0 * lda2;
-    ca = (const char*)g.a.base[0] + a_row0;
-    cb = (const char*)g.B + n0 * 2;
-    ct = 0; cs = 0; cts = 0; cft = 0; cfsub = 0;
-    gate(0);
+    // A segment starts at a shard border: kb = cs * SPS.
+    ct = cseg.kb;
+    cs = cseg.kb / SPS;
+    cts = 0;
+    cft = cs * g.gate.kt;
+    cfsub = 0;
+    ca = (const char*)g.a.base[cs] + a_row0;
+    cb = (const char*)g.B + n0 * 2 + (int64_t)cseg.kb * BK * N * 2;
+    gate(cft);
   };
   auto cursor_advance = [&]() {
-    if (++ct == NS) {
-      const int nw = cw + G;
-      if (nw < total) {
-        cw = nw;
-        cursor_enter(cw);
-      } else {
-        ct = NS - 1;
-      }
+    if (++ct == cseg.ke) {
+      if (seg_next(cseg)) cursor_enter();
+      else ct = cseg.ke - 1;
       return;
     }
     cb += (int64_t)BK * N * 2;
@@ -377,15 +443,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     bool up = false;
     if (lane < g.gate.t) up = (int32_t)(g.gate.flags[lane] - g.gate.target) >= 0;
     const uint64_t mask = __ballot(up);
-    ready = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mask >> 32)) << 32) |
-            (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)mask);
+    ready = uniform_mask(mask);
     if (g.gate.strict) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     asm volatile("" ::: "memory");
   }
 
   // Prologue: steps 0 .. STAGES-2 in full; the interval opened by the
   // prologue barrier then loads step STAGES-1 into the last buffer.
-  cursor_enter(cw);
+  cursor_enter();
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p) {
 #pragma unroll
@@ -400,9 +465,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) read_one_ks<BM, BN, BK, WM, WN>(0, r, lds0, ra_ks, rb, F0);
 
+  // Split-K hand-off (SPLIT only). Owner of unit u: the largest b with
+  // floor(b*U/G) <= u. Each workgroup publishes at most two partials, for its
+  // first and its last tile, in slots 2*b and 2*b + 1; one ticket counter per
+  // tile.
+  __shared__ uint32_t s_ticket;
+  auto owner = [&](int64_t u) { return (int)(((u + 1) * G - 1) / U); };
+  auto slot_of = [&](int b, int w) {
+    const int first_tile = (int)(((int64_t)b * U / G) / Wsh);
+    return 2 * b + (first_tile == w ? 0 : 1);
+  };
+  constexpr int SLOT_U64 = BM * BN / 2;  // one slot in 8-byte words
+  // Word h of block (fm, fn) of thread tid: contiguous across the workgroup.
+  auto slot_word = [&](int fm, int fn, int h) { return ((fm * FN + fn) * 8 + h) * NT + tid; };
+
   auto main_loop = [&]() {
     int buf = 0;
-    for (int w = blockIdx.x; w < total; w += G) {
+    Seg ms;
+    seg_first(ms);
+    do {
+      const int w = ms.w;
       f32x16 acc[FM][FN];
   #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -411,7 +493,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   #pragma unroll
           for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-      for (int t = 0; t < NS; ++t) {
+      for (int t = ms.kb; t < ms.ke; ++t) {
         const uint32_t cur = lds0 + buf * S::STAGE;
         const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
         // Substeps 0 .. KSUB-2: MFMAs of this substep, with the next substep's
@@ -459,6 +541,76 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
         // the assembler MFMAs' results are read below: let the last ones retire
         asm volatile("s_nop 15\n s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
       }
+      // A tile whose units fall to several workgroups: each publishes its
+      // partial sums (device-coherent stores, which bypass the per-XCD L2s),
+      // waits until they have completed, and then counts itself in with one
+      // atomic; the workgroup that counts in last already sees every other
+      // partial, adds all of them in contributor order (its own from its
+      // registers) and writes C. Nobody waits for anybody, and the result
+      // does not depend on which workgroup finishes last. (A variant in
+      // which only the non-last contributors published, and the last polled
+      // a publication counter, failed on MI355X: the poll kept reading a
+      // stale count while the others' increments landed.)
+      bool reduce = false;
+      int gfirst = 0, ncontrib = 1;
+      if constexpr (SPLIT) {
+        if (ms.kb != 0 || ms.ke != NS) {
+          const int64_t uf = (int64_t)w * Wsh;
+          gfirst = owner(uf);
+          ncontrib = owner(uf + Wsh - 1) - gfirst + 1;
+          uint64_t* dst = reinterpret_cast<uint64_t*>(g.split_ws) + (int64_t)slot_of(bp, w) * SLOT_U64;
+  #pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+  #pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+  #pragma unroll
+              for (int h = 0; h < 8; ++h) {
+                // copy the elements out first: a bit cast applied to a vector
+                // element itself was compiled as a read of element 0
+                const float lo = acc[fm][fn][2 * h], hi = acc[fm][fn][2 * h + 1];
+                store_coherent(dst + slot_word(fm, fn, h), ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32) |
+                                                               __builtin_bit_cast(uint32_t, lo));
+              }
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          uint32_t* cnt = g.split_cnt + w;
+          if (tid == 0) s_ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __syncthreads();
+          const uint32_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+          if (ticket + 1 != (uint32_t)ncontrib) continue;
+          // every contributor has counted in: clear the counter for the next call
+          if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          reduce = true;
+        }
+      }
+      // Sum of block (fm, fn) over the contributors in order, this
+      // workgroup's own partial taken from its registers.
+      auto total_of = [&](int fm, int fn) -> f32x16 {
+        f32x16 v = acc[fm][fn];
+        if constexpr (SPLIT) {
+          if (reduce) {
+            const int me = bp - gfirst;
+            for (int j = 0; j < ncontrib; ++j) {
+              f32x16 p;
+              if (j == me) {
+                p = acc[fm][fn];
+              } else {
+                const uint64_t* src =
+                    reinterpret_cast<const uint64_t*>(g.split_ws) + (int64_t)slot_of(gfirst + j, w) * SLOT_U64;
+  #pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                  const uint64_t x = load_coherent(src + slot_word(fm, fn, h));
+                  p[2 * h] = __builtin_bit_cast(float, (uint32_t)x);
+                  p[2 * h + 1] = __builtin_bit_cast(float, (uint32_t)(x >> 32));
+                }
+              }
+              if (j == 0) v = p;
+              else v = v + p;
+            }
+          }
+        }
+        return v;
+      };
       int64_t m0, n0;
       tile_coords(w, m0, n0);
       const int64_t col0 = n0 + wn * TN + (lane >> 5) * 4;
@@ -472,12 +624,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
             __builtin_amdgcn_sched_barrier(0);
+            const f32x16 v = total_of(fm, fn);
   #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int c = fn * 32 + q * 8;
               if (!full && col0 + c >= N) continue;
-              *reinterpret_cast<float4*>(row + c) = make_float4(acc[fm][fn][q * 4 + 0], acc[fm][fn][q * 4 + 1],
-                                                                acc[fm][fn][q * 4 + 2], acc[fm][fn][q * 4 + 3]);
+              *reinterpret_cast<float4*>(row + c) =
+                  make_float4(v[q * 4 + 0], v[q * 4 + 1], v[q * 4 + 2], v[q * 4 + 3]);
             }
           }
         } else {
@@ -485,13 +638,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
             __builtin_amdgcn_sched_barrier(0);  // convert one accumulator block at a time
+            const f32x16 tv = total_of(fm, fn);
   #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int c = fn * 32 + q * 8;
               if (!full && col0 + c >= N) continue;
               uint2 v;
-              float x0 = acc[fm][fn][q * 4 + 0], x1 = acc[fm][fn][q * 4 + 1];
-              float x2 = acc[fm][fn][q * 4 + 2], x3 = acc[fm][fn][q * 4 + 3];
+              float x0 = tv[q * 4 + 0], x1 = tv[q * 4 + 1];
+              float x2 = tv[q * 4 + 2], x3 = tv[q * 4 + 3];
               asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(v.x) : "v"(x0), "v"(x1));
               asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(v.y) : "v"(x2), "v"(x3));
               *reinterpret_cast<uint2*>(row + c) = v;
@@ -499,33 +653,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
           }
         }
       }
-    }
+    } while (seg_next(ms));
   };
   main_loop();
   __builtin_amdgcn_s_waitcnt(0);
 }
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN>
-hipError_t launch_cfg(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
-  const int64_t MB = (a.M + BM - 1) / BM;
-  const int64_t NB = (a.N + BN - 1) / BN;
+hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   // Persistent grid of at most one workgroup per CU (the LDS ring admits no
   // second one). Every configuration leaves registers free on each SIMD, so
   // producer workgroups can always run beside spinning consumers.
-  const int64_t tiles = MB * NB;
-  const int64_t g = tiles < a.num_cus ? tiles : a.num_cus;
-  const dim3 grid((unsigned)g), block(64 * WM * WN);
+  if (p.bm != BM || p.bn != BN) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)p.grid), block(64 * WM * WN);
   const bool gated = a.gate.flags != nullptr;
-#define L(G_, F_)                                                                                        \
-  do {                                                                                                  \
-    if (t.start)                                                                                        \
-      hipExtLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_>), grid, block, 0, s, t.start, \
-                            t.stop, 0, a);                                                              \
-    else                                                                                                \
-      hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_>), grid, block, 0, s, a);   \
+#define L(G_, F_, S_)                                                                                     \
+  do {                                                                                                   \
+    if (t.start)                                                                                         \
+      hipExtLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_>), grid, block, 0, s, \
+                            t.start, t.stop, 0, a);                                                      \
+    else                                                                                                 \
+      hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_>), grid, block, 0, s, a);  \
   } while (0)
-  if (gated) { if (out_f32) L(true, true); else L(true, false); }
-  else { if (out_f32) L(false, true); else L(false, false); }
+#define L2(S_)                                                     \
+  do {                                                             \
+    if (gated) { if (out_f32) L(true, true, S_); else L(true, false, S_); }   \
+    else { if (out_f32) L(false, true, S_); else L(false, false, S_); }       \
+  } while (0)
+  if (p.split) L2(true);
+  else L2(false);
+#undef L2
 #undef L
   return hipGetLastError();
 }
@@ -539,12 +696,43 @@ int mfma_config_for(int64_t M, int tile_config) {
   return M > 192 ? 0 : 2;
 }
 
+MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode) {
+  MfmaPlan p;
+  p.cfg = mfma_config_for(M, tile_config);
+  p.bm = p.cfg == 2 ? 128 : 256;
+  p.bn = p.bm;
+  p.tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  // Busiest workgroup's run, in (tile, shard) units: whole tiles dealt to
+  // min(tiles, CUs) workgroups, against equal runs of units over min(units, CUs).
+  // Every split tile costs its contributors a BM x BN fp32 partial each
+  // (written and read back once); measured on MI355X at K = 8192, N = 28672,
+  // that hand-off outweighs a 12.5 % shorter run (224 tiles on 256 CUs: 120
+  // against 101 us at M = 128, 333 against 245 us at M = 512). The automatic
+  // choice therefore splits only when whole tiles would leave at least half
+  // of the CUs idle, where the run shrinks by 2x or more.
+  const int64_t g_tiles = std::min<int64_t>(p.tiles, num_cus);
+  const int64_t run_tiles = (p.tiles + g_tiles - 1) / g_tiles * W;
+  const int64_t units = p.tiles * W;
+  const int64_t g_units = std::min<int64_t>(units, num_cus);
+  const int64_t run_units = (units + g_units - 1) / g_units;
+  if (split_mode < 0) p.split = W >= 2 && 2 * p.tiles <= num_cus && 2 * run_units <= run_tiles;
+  else p.split = split_mode > 0 && W >= 2;
+  p.grid = p.split ? g_units : g_tiles;
+  if (p.split) {
+    p.ws_bytes = sizeof(float) * 2 * (size_t)p.grid * (size_t)(p.bm * p.bn);
+    p.cnt_bytes = sizeof(uint32_t) * (size_t)p.tiles;
+  }
+  return p;
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
-  switch (mfma_config_for(a.M, a.tile_config)) {
-    case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, out_f32, s, t);   // 4 waves, 128x128 per wave
-    case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, out_f32, s, t);   // 8 waves, 128x64 per wave
-    case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, out_f32, s, t);   // 4 waves, 64x64 per wave
-    default: return launch_cfg<256, 256, 32, 4, 2, 4>(a, out_f32, s, t);  // 8 waves, 128x64, BK 32
+  MfmaPlan p = mfma_plan(a.M, a.N, a.W, a.num_cus, a.tile_config, a.split ? 1 : 0);
+  if (p.split && (!a.split_ws || !a.split_cnt)) return hipErrorInvalidValue;
+  switch (p.cfg) {
+    case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 128x128 per wave
+    case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, p, out_f32, s, t);   // 8 waves, 128x64 per wave
+    case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 64x64 per wave
+    default: return launch_cfg<256, 256, 32, 4, 2, 4>(a, p, out_f32, s, t);  // 8 waves, 128x64, BK 32
   }
 }
 

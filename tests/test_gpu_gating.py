@@ -180,6 +180,40 @@ def test_call_order_and_argument_errors():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("split", ["0", "1"])
+def test_flag_tiles_above_31_wait_when_tile_31_is_up(split, monkeypatch):
+    """T = 64 flags: tiles 0..31 (tile 31 first) are released at once, tiles 32..63 two
+    milliseconds later, into poisoned inboxes. A wave's 64-bit record of raised flags
+    must not carry bit 31 into bits 32..63 (a sign-extended low half would mark every
+    later tile raised and read them before their data). Whole tiles and the stream-K
+    split, which starts workgroups at shards 4..7 (tiles 32..63)."""
+    import torch
+    from shard_decomposed_gemm_amd import Context
+    monkeypatch.setenv("AGEMM_SPLIT", split)
+    W, M, K, N, bkf = 8, 300, 8192, 1000, 128
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=47)
+    ref = oracle.sharded_gemm(sh, b)
+    ctx = Context(W, M, K, N, c_dtype="f32", flag_ktile=bkf)
+    assert ctx.t == 64 and ctx.split is (split == "1")
+    order = np.array([31] + list(range(31)) + list(range(32, 64)), dtype=np.int32)
+    offs = np.array([0] * 32 + [2_000_000 + 1_000 * i for i in range(32)], dtype=np.int64)
+    nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        ctx.produce(nan)
+        ctx.produce(nan)
+        torch.cuda.synchronize()
+        C = gu.empty_c(M, N, "f32")
+        ctx.produce(dsh, schedule=(order, offs), stream=sp)
+        ctx.run_fused(B, C, stream=sc)
+        torch.cuda.synchronize()
+        ctx.check()
+        got = gu.c_to_f64(C)
+        assert np.isfinite(got).all()
+        assert np.abs(got - ref).max() <= oracle.tolerance(K)
+    ctx.close()
+
+
 @pytest.mark.parametrize("M,epochs", [(1, 120), (7, 120), (300, 120), (1024, 120), (512, 1000)])
 def test_epoch_stress_bitwise(M, epochs, gate_mode):
     """120 (at M = 512: 1000) epochs cycle three data sets with jittered release schedules while the
