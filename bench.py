@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps, so the engine clock has settled")
+    ap.add_argument("--order", choices=["shard", "arrival"], default="shard",
+                    help="flag-tile order of the fused consumer (agemm_set_order)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
@@ -301,6 +303,7 @@ def main():
     c_bytes = 2 if c_dtype == "f16" else 4
     Cs = [torch.empty((M, N), dtype=cdt, device=dev) for _ in range(2)]
     ctx = Context(W, M, K, N, c_dtype=c_dtype)
+    ctx.set_order(args.order)
     sched = synth.schedule(0x5005, ctx.t, 20_000) if sched_kind == "random" else None
     sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
     if args.one_stream:
@@ -416,7 +419,7 @@ def main():
         "config": {"workload": args.workload, "W": W, "M": M, "K": K, "N": N, "c_dtype": c_dtype,
                    "accumulate": "f32", "flag_ktile": ctx.bkf, "tiles": ctx.t,
                    "schedule": "seeded permutation, cumulative U[0,20] us delays" if sched else "shard order, no delay",
-                   "path": "producer || flag-gated consumer on two streams"},
+                   "path": "producer || flag-gated consumer on two streams", "order": args.order},
         "roofline": roof,
         "cpu_baseline": cpu,
         "ladder": ladder,

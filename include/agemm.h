@@ -85,6 +85,12 @@ typedef enum {
 
 typedef enum { AGEMM_F16 = 0, AGEMM_F32 = 1 } agemm_dtype;
 
+/* Order in which the fused consumer takes an output tile's flag tiles. */
+typedef enum {
+  AGEMM_ORDER_SHARD = 0,   /* s = 0..W-1, k-tiles ascending (the core identity's loop order) */
+  AGEMM_ORDER_ARRIVAL = 1  /* raised ones first, see agemm_set_order */
+} agemm_order;
+
 /* Release schedule of the producer (host arrays, read during the call only).
  * order[p] is the tile id released p-th; offset_ns[p] is its release time in
  * nanoseconds after the producer starts, non-decreasing in p. n must equal T
@@ -153,6 +159,18 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
 /* Pull model on one GPU: the GEMM reads every K-slice straight from the W
  * shard buffers; no inbox, no flags, one kernel. */
 int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, void* stream);
+
+/* Flag-tile order of later agemm_run_fused calls (default AGEMM_ORDER_SHARD).
+ * The AG+GEMM core identity is a plain sum over shards, so the shards' k-tiles
+ * may be added in any order. With AGEMM_ORDER_ARRIVAL each output tile takes
+ * first, in ascending id, the flag tiles already raised when the consumer
+ * reaches it, then the rest in ascending id (each still waited for), so a late
+ * shard delays only the work that needs it. Exact-arithmetic results are
+ * unchanged; fp32 rounding may differ from shard order. Runs on whole tiles
+ * (the stream-K split, if the context chose it, is not used for these calls)
+ * and on the MFMA consumer only; the small-M consumer keeps every K-range
+ * resident at once and needs no reordering. EINVAL for an unknown order. */
+int agemm_set_order(agemm_ctx* ctx, int order);
 
 /* Sets the consumer's spin timeout in microseconds (default 2,000,000, or
  * the AGEMM_SPIN_TIMEOUT_MS environment variable at create time). */

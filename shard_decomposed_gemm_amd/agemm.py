@@ -20,7 +20,7 @@ F16, F32 = 0, 1
 
 EXPORTED = (
     "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_produce", "agemm_run_fused",
-    "agemm_run_bsp", "agemm_run_pull", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
+    "agemm_run_bsp", "agemm_run_pull", "agemm_set_order", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
     "agemm_check",
     "agemm_last_error", "agemm_status_string",
 )
@@ -57,6 +57,7 @@ def load() -> ctypes.CDLL:
     lib.agemm_run_fused.argtypes = [vp, vp, vp, vp]
     lib.agemm_run_bsp.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Schedule), ctypes.c_int, vp]
     lib.agemm_run_pull.argtypes = [vp, vp, vp, vp, vp]
+    lib.agemm_set_order.argtypes = [vp, ctypes.c_int]
     lib.agemm_set_spin_timeout_us.argtypes = [vp, i64]
     lib.agemm_timing_begin.argtypes = [vp, i32]
     lib.agemm_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
@@ -181,6 +182,13 @@ class Context:
         arr = self._shards(a_shards)
         b, c = self._bc(B, C)
         self._raise(self._lib.agemm_run_pull(self._h, arr, b, c, _stream_handle(stream)), "agemm_run_pull")
+
+    def set_order(self, order: str):
+        """Flag-tile order of later run_fused calls: "shard" or "arrival" (agemm_set_order)."""
+        code = {"shard": 0, "arrival": 1}.get(order)
+        if code is None:
+            raise ValueError("order must be 'shard' or 'arrival'")
+        self._raise(self._lib.agemm_set_order(self._h, code), "agemm_set_order")
 
     def set_spin_timeout_us(self, us: int):
         self._raise(self._lib.agemm_set_spin_timeout_us(self._h, int(us)), "agemm_set_spin_timeout_us")

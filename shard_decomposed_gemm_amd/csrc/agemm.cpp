@@ -27,6 +27,7 @@ struct agemm_ctx {
   int device = 0;
   int num_cus = 0;
   int tile_config = -1;  // AGEMM_TILE_CONFIG override of the MFMA tile choice
+  int order = AGEMM_ORDER_SHARD;  // flag-tile order of the fused consumer (agemm_set_order)
   int strict_acquire = 0;  // AGEMM_STRICT_ACQUIRE=1: agent-scope acquire fence after flag waits
   double ticks_per_ns = 0.1;  // wall clock (kHz / 1e6)
   uint64_t timeout_ticks = 0;
@@ -183,6 +184,7 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.tile_config = c->tile_config;
   g.gate = gate;
   g.split = c->mplan.split ? 1 : 0;
+  g.arrival = (gate.flags != nullptr && c->order == AGEMM_ORDER_ARRIVAL) ? 1 : 0;
   g.split_ws = c->mws;
   g.split_cnt = c->mcnt;
   const bool f32 = c->c_dtype == AGEMM_F32;
@@ -424,6 +426,13 @@ int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split) {
   const bool small = ctx->ws != nullptr;
   if (grid) *grid = small ? -1 : (int32_t)ctx->mplan.grid;
   if (split) *split = small ? 0 : (ctx->mplan.split ? 1 : 0);
+  return AGEMM_OK;
+}
+
+int agemm_set_order(agemm_ctx* ctx, int order) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (order != AGEMM_ORDER_SHARD && order != AGEMM_ORDER_ARRIVAL) return fail(ctx, AGEMM_EINVAL, "unknown order %d", order);
+  ctx->order = order;
   return AGEMM_OK;
 }
 

@@ -51,6 +51,9 @@ struct GemmArgs {
   int32_t split;
   float* split_ws;      // 2 * grid slots of BM x BN fp32 partials
   uint32_t* split_cnt;  // one ticket counter per output tile, zero between calls
+  // Gated launches only: 1 = take each output tile's flag tiles in arrival
+  // order (raised ones first), 0 = shard order.
+  int32_t arrival;
 };
 
 // Launch plan of the MFMA consumer for a shape, fixed when a context is

@@ -188,8 +188,9 @@ __device__ inline uint64_t load_coherent(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool GATED, bool OUTF32, bool SPLIT>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool GATED, bool OUTF32, bool SPLIT, bool ARRIVAL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
+  static_assert(!ARRIVAL || (GATED && !SPLIT), "arrival order is a mode of the gated whole-tile consumer");
   using S = Shape<BM, BN, BK, WM, WN>;
   constexpr int NT = S::NT, TM = S::TM, TN = S::TN, FM = S::FM, FN = S::FN, LOADS = S::LOADS;
   constexpr int CPR_A = S::CPR_A, CPR_B = S::CPR_B, KSUB = S::KSUB, NMF = S::NMF, NR = S::NR, LPS = S::LPS;
@@ -307,6 +308,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   // barrier sequence, and C is undefined.
   uint64_t ready = 0;
   bool dead = false;
+  // Arrival order (ARRIVAL only). The sum over shards may be taken in any
+  // order, so per output tile the flag tiles already raised when the cursor
+  // enters it go first (ascending), then the others (ascending), each still
+  // gated. Wave 0 takes the look and publishes it through LDS; the other
+  // waves read it after the next workgroup barrier, so every wave loads the
+  // same flag tile into each stage.
+  __shared__ uint64_t s_snap;
+  uint64_t snap = 0, taken = 0;
+  bool pending = false;  // entered a tile whose order is applied after the next barrier
+  int64_t c_n0 = 0;
+  const uint64_t tmask = g.gate.t >= 64 ? ~0ull : ((1ull << g.gate.t) - 1ull);
   auto gate = [&](const int tile) {
     if constexpr (GATED) {
       // Fast path (tile already seen, or given up) falls through without a
@@ -388,6 +400,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       b_off[j] = (uint32_t)((k * N + c) * 2);
     }
     a_row0 = m0 * lda2;
+    if constexpr (ARRIVAL) {
+      c_n0 = n0;
+      ct = 0;
+      cfsub = 0;
+      if (wave == 0) {
+        bool up = false;
+        if (lane < g.gate.t)
+          up = (int32_t)(__hip_atomic_load(const_cast<uint32_t*>(g.gate.flags) + lane, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) - g.gate.target) >= 0;
+        const uint64_t m = uniform_mask(__ballot(up));
+        if (lane == 0) s_snap = m;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      pending = true;
+      return;
+    }
     // A segment starts at a shard border: kb = cs * SPS.
     ct = cseg.kb;
     cs = cseg.kb / SPS;
@@ -398,10 +426,41 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     cb = (const char*)g.B + n0 * 2 + (int64_t)cseg.kb * BK * N * 2;
     gate(cft);
   };
+  // Arrival order: the next flag tile of the current output tile; points the
+  // cursor at its first k-step and gates it. Called T times per tile, so an
+  // untaken tile always remains.
+  auto next_flag_tile = [&]() {
+    uint64_t c = snap & ~taken & tmask;
+    if (c == 0) c = ~taken & tmask;
+    const int f = (int)__builtin_ctzll(c);
+    taken |= 1ull << f;
+    cft = f;
+    const int fs = f / g.gate.kt, fk = f - fs * g.gate.kt;
+    ca = (const char*)g.a.base[fs] + a_row0 + (int64_t)fk * spt * BK * 2;
+    cb = (const char*)g.B + c_n0 * 2 + ((int64_t)fs * SPS + (int64_t)fk * spt) * BK * N * 2;
+    gate(f);
+  };
+  auto arrival_apply = [&]() {
+    snap = uniform_mask(s_snap);
+    ready |= snap;
+    taken = 0;
+    pending = false;
+    next_flag_tile();
+  };
   auto cursor_advance = [&]() {
     if (++ct == cseg.ke) {
       if (seg_next(cseg)) cursor_enter();
       else ct = cseg.ke - 1;
+      return;
+    }
+    if constexpr (ARRIVAL) {
+      if (++cfsub == spt) {
+        cfsub = 0;
+        next_flag_tile();
+      } else {
+        cb += (int64_t)BK * N * 2;
+        ca += BK * 2;
+      }
       return;
     }
     cb += (int64_t)BK * N * 2;
@@ -451,6 +510,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   // Prologue: steps 0 .. STAGES-2 in full; the interval opened by the
   // prologue barrier then loads step STAGES-1 into the last buffer.
   cursor_enter();
+  if constexpr (ARRIVAL) {
+    barrier();
+    arrival_apply();
+  }
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p) {
 #pragma unroll
@@ -459,6 +522,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   }
   wait_vmcnt<(STAGES - 2) * LOADS>();
   barrier();
+  if constexpr (ARRIVAL) {
+    if (pending) arrival_apply();
+  }
   int dbuf = STAGES - 1;  // buffer the current interval's direct loads go to
 #pragma unroll
   for (int j = 0; j < LPS; ++j) issue_one(j, dbuf);
@@ -523,6 +589,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
         wait_frags(fl);
         wait_vmcnt<(STAGES - 2) * LOADS>();
         barrier();
+        if constexpr (ARRIVAL) {
+          if (pending) arrival_apply();
+        }
         dbuf = buf;
         const uint32_t nxt = lds0 + nbuf * S::STAGE;
   #pragma unroll
@@ -659,6 +728,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+inline bool arrival_requested(const GemmArgs& a) { return a.arrival != 0 && a.gate.flags != nullptr; }
+
 template <int BM, int BN, int BK, int STAGES, int WM, int WN>
 hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   // Persistent grid of at most one workgroup per CU (the LDS ring admits no
@@ -667,23 +738,34 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
   if (p.bm != BM || p.bn != BN) return hipErrorInvalidValue;
   const dim3 grid((unsigned)p.grid), block(64 * WM * WN);
   const bool gated = a.gate.flags != nullptr;
-#define L(G_, F_, S_)                                                                                     \
-  do {                                                                                                   \
-    if (t.start)                                                                                         \
-      hipExtLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_>), grid, block, 0, s, \
-                            t.start, t.stop, 0, a);                                                      \
-    else                                                                                                 \
-      hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_>), grid, block, 0, s, a);  \
+  // Arrival order needs a tile to span at least the prologue's steps (the
+  // cursor publishes a tile's order at a barrier the prologue does not have).
+  const bool arrival = arrival_requested(a) && !p.split && a.K / BK >= STAGES;
+#define L4(G_, F_, S_, A_)                                                                                     \
+  do {                                                                                                        \
+    if (t.start)                                                                                              \
+      hipExtLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_, A_>), grid, block, 0, s,  \
+                            t.start, t.stop, 0, a);                                                           \
+    else                                                                                                      \
+      hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_, A_>), grid, block, 0, s, a); \
   } while (0)
+#define L(G_, F_, S_) L4(G_, F_, S_, false)
 #define L2(S_)                                                     \
   do {                                                             \
     if (gated) { if (out_f32) L(true, true, S_); else L(true, false, S_); }   \
     else { if (out_f32) L(false, true, S_); else L(false, false, S_); }       \
   } while (0)
-  if (p.split) L2(true);
-  else L2(false);
+  if (arrival) {
+    if (out_f32) L4(true, true, false, true);
+    else L4(true, false, false, true);
+  } else if (p.split) {
+    L2(true);
+  } else {
+    L2(false);
+  }
 #undef L2
 #undef L
+#undef L4
   return hipGetLastError();
 }
 
@@ -726,7 +808,8 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, in
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
-  MfmaPlan p = mfma_plan(a.M, a.N, a.W, a.num_cus, a.tile_config, a.split ? 1 : 0);
+  // Arrival order runs on whole tiles (a split tile's partial ranges stay in shard order).
+  MfmaPlan p = mfma_plan(a.M, a.N, a.W, a.num_cus, a.tile_config, (a.split && !arrival_requested(a)) ? 1 : 0);
   if (p.split && (!a.split_ws || !a.split_cnt)) return hipErrorInvalidValue;
   switch (p.cfg) {
     case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 128x128 per wave

@@ -6,8 +6,10 @@ shards may be taken in any order; the consumer in arrival order takes, per
 output tile, the raised flag tiles first. Checks: exact inputs give the
 oracle bit for bit in any order; random inputs stay within the tolerance; a
 poisoned inbox is never read early; with every flag up at launch the result
-equals the shard-order one bit for bit; and a late first shard costs the
-arrival-order consumer only the tail of the work.
+equals the shard-order one bit for bit; a late first shard costs the
+arrival-order consumer only the tail of the work; and with 64 flag tiles the
+order never reaches past the last tile (a sign-extended 64-bit record of
+raised flags once made tiles 32..63 look raised).
 """
 import numpy as np
 import pytest
@@ -16,13 +18,14 @@ import oracle
 import synth
 from tests import gpu_util as gu
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="arrival-order consumption is switched off: the late-first-shard case "
-                            "(M=1024, K=8192, N=8192, shard 0 released 3 ms after the rest) ended in a GPU "
-                            "memory fault whose cause has not been found; the consumer runs in shard order "
-                            "only and agemm_set_order is not exported until the cause is shown"),
-]
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _whole_tiles(monkeypatch):
+    """Arrival order runs on whole tiles; the shard-order contexts these tests compare
+    with are kept on whole tiles too (the stream-K split groups the sum differently)."""
+    monkeypatch.setenv("AGEMM_SPLIT", "0")
 
 
 def _ctx(W, M, K, N, c_dtype="f32", order="arrival"):
@@ -173,3 +176,28 @@ def test_arrival_late_first_shard_costs_only_the_tail():
     if dur["shard"] < 2_500:
         pytest.skip("producer and consumer did not overlap (the consumer never waited)")
     assert dur["arrival"] < dur["shard"] - 0.5 * gemm_us
+
+
+def test_arrival_sixty_four_flags_late_high_tiles():
+    """T = 64: tiles 0..31 (tile 31 first) released at once, tiles 32..63 two milliseconds
+    later, into poisoned inboxes. The arrival order takes the raised tiles first and must
+    then wait for each of 32..63, never take a tile it has not seen raised, and never
+    pick an id at or beyond T."""
+    import torch
+    W, M, K, N, bkf = 8, 300, 8192, 1000, 128
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=49)
+    ref = oracle.sharded_gemm(sh, b)
+    from shard_decomposed_gemm_amd import Context
+    ctx = Context(W, M, K, N, c_dtype="f32", flag_ktile=bkf)
+    ctx.set_order("arrival")
+    assert ctx.t == 64
+    order = np.array([31] + list(range(31)) + list(range(32, 64)), dtype=np.int32)
+    offs = np.array([0] * 32 + [2_000_000 + 1_000 * i for i in range(32)], dtype=np.int64)
+    for _ in range(3):
+        _poison(ctx, W, M, K)
+        C = gu.empty_c(M, N, "f32")
+        _fused_concurrent(ctx, dsh, B, C, (order, offs))
+        got = gu.c_to_f64(C)
+        assert np.isfinite(got).all()
+        assert np.abs(got - ref).max() <= oracle.tolerance(K)
+    ctx.close()
