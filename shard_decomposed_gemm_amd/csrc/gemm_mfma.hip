@@ -309,14 +309,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   uint64_t ready = 0;
   bool dead = false;
   // Arrival order (ARRIVAL only). The sum over shards may be taken in any
-  // order, so per output tile the flag tiles already raised when the cursor
-  // enters it go first (ascending), then the others (ascending), each still
-  // gated. Wave 0 takes the look and publishes it through LDS; the other
-  // waves read it after the next workgroup barrier, so every wave loads the
-  // same flag tile into each stage.
-  __shared__ uint64_t s_snap;
-  uint64_t snap = 0, taken = 0;
-  bool pending = false;  // entered a tile whose order is applied after the next barrier
+  // order, so at each flag-tile boundary of an output tile wave 0 picks the
+  // lowest-numbered flag tile it has seen raised and not yet taken (polling
+  // only when there is none) and publishes the choice through LDS; every
+  // wave applies it after the next workgroup barrier, so all waves load the
+  // same flag tile into each stage. Two alternating slots: a choice is
+  // written only after every wave has passed the barrier that follows the
+  // read of the choice before it.
+  __shared__ int s_choice[2];
+  uint64_t taken = 0;
+  int wslot = 0, rslot = 0;
+  bool pending = false;  // a choice waits to be applied after the next barrier
   int64_t c_n0 = 0;
   const uint64_t tmask = g.gate.t >= 64 ? ~0ull : ((1ull << g.gate.t) - 1ull);
   auto gate = [&](const int tile) {
@@ -375,6 +378,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     m0 = (int64_t)(first_m + in_group % gsize) * BM;
     n0 = (int64_t)(in_group / gsize) * BN;
   };
+  // Arrival order: wave 0's choice of the next flag tile (see above). If no
+  // untaken tile comes up within the timeout it takes the lowest untaken one,
+  // whose gate then reports the timeout.
+  auto choose = [&]() {
+    if constexpr (ARRIVAL) {
+      if (wave == 0) {
+        uint64_t c = ready & ~taken & tmask;
+        if (c == 0 && !dead) {
+          const uint64_t start = wall_clock();
+          while (true) {
+            bool up = false;
+            if (lane < g.gate.t)
+              up = (int32_t)(__hip_atomic_load(const_cast<uint32_t*>(g.gate.flags) + lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) - g.gate.target) >= 0;
+            ready |= uniform_mask(__ballot(up));
+            c = ready & ~taken & tmask;
+            if (c != 0 || wall_clock() - start > g.gate.timeout_ticks) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        if (c == 0) c = ~taken & tmask;
+        if (lane == 0) s_choice[wslot] = (int)__builtin_ctzll(c);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      wslot ^= 1;
+      pending = true;
+    }
+  };
   // Lane offsets of tile w: the LDS destination of chunk q is byte q*16 of
   // the stage; rows past M and columns past N re-load a valid row/column
   // whose results are never stored. m0 and n0 go into the base pointers.
@@ -404,16 +435,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       c_n0 = n0;
       ct = 0;
       cfsub = 0;
-      if (wave == 0) {
-        bool up = false;
-        if (lane < g.gate.t)
-          up = (int32_t)(__hip_atomic_load(const_cast<uint32_t*>(g.gate.flags) + lane, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) - g.gate.target) >= 0;
-        const uint64_t m = uniform_mask(__ballot(up));
-        if (lane == 0) s_snap = m;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      }
-      pending = true;
+      taken = 0;
+      choose();
       return;
     }
     // A segment starts at a shard border: kb = cs * SPS.
@@ -426,26 +449,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     cb = (const char*)g.B + n0 * 2 + (int64_t)cseg.kb * BK * N * 2;
     gate(cft);
   };
-  // Arrival order: the next flag tile of the current output tile; points the
-  // cursor at its first k-step and gates it. Called T times per tile, so an
-  // untaken tile always remains.
-  auto next_flag_tile = [&]() {
-    uint64_t c = snap & ~taken & tmask;
-    if (c == 0) c = ~taken & tmask;
-    const int f = (int)__builtin_ctzll(c);
+  // Arrival order: applies the published choice (after a barrier): points the
+  // cursor at the flag tile's first k-step and gates it. The choice is one of
+  // the tile's untaken flag tiles (masked with T), so every k-step of the
+  // output tile is loaded exactly once.
+  auto arrival_apply = [&]() {
+    const int f = __builtin_amdgcn_readfirstlane(s_choice[rslot]);
+    rslot ^= 1;
+    pending = false;
     taken |= 1ull << f;
     cft = f;
     const int fs = f / g.gate.kt, fk = f - fs * g.gate.kt;
     ca = (const char*)g.a.base[fs] + a_row0 + (int64_t)fk * spt * BK * 2;
     cb = (const char*)g.B + c_n0 * 2 + ((int64_t)fs * SPS + (int64_t)fk * spt) * BK * N * 2;
     gate(f);
-  };
-  auto arrival_apply = [&]() {
-    snap = uniform_mask(s_snap);
-    ready |= snap;
-    taken = 0;
-    pending = false;
-    next_flag_tile();
   };
   auto cursor_advance = [&]() {
     if (++ct == cseg.ke) {
@@ -456,7 +473,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     if constexpr (ARRIVAL) {
       if (++cfsub == spt) {
         cfsub = 0;
-        next_flag_tile();
+        choose();
       } else {
         cb += (int64_t)BK * N * 2;
         ca += BK * 2;
@@ -519,6 +536,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) issue_one(j, p);
     cursor_advance();
+    if constexpr (ARRIVAL) {
+      if (pending) {
+        barrier();
+        arrival_apply();
+      }
+    }
   }
   wait_vmcnt<(STAGES - 2) * LOADS>();
   barrier();
