@@ -129,6 +129,18 @@ int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
  * pointer may be NULL. */
 int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_config);
 
+/* The MFMA consumer's work plan for a shape on a GPU with num_cus compute
+ * units, computed on the host without a device (the choice agemm_create
+ * makes): *cfg = tile configuration 0..3, *grid = workgroups of the
+ * persistent grid, *split = 1 for the stream-K split. tile_config -1 and
+ * split_mode -1 are the automatic choices (AGEMM_TILE_CONFIG / AGEMM_SPLIT
+ * give the others). Applies to the MFMA consumer only (a context with
+ * M <= 8 uses the small-M kernel). EINVAL for M < 1, N < 8, W outside
+ * 1..16, num_cus < 1 or an out-of-range tile_config / split_mode. Output
+ * pointers may be NULL. */
+int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
+                    int32_t* grid, int32_t* split);
+
 /* Launch shape of the MFMA consumer: *grid = its workgroups, *split = 1 when
  * it runs the stream-K split described above, else 0. For the small-M kernel
  * *grid = -1 and *split = 0. Either output pointer may be NULL. */

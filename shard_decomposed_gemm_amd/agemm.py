@@ -19,7 +19,7 @@ OK, EINVAL, ESHAPE, ENOMEM, EHIP, ETIMEOUT, ESTATE = range(7)
 F16, F32 = 0, 1
 
 EXPORTED = (
-    "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_produce", "agemm_run_fused",
+    "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_mfma_plan", "agemm_produce", "agemm_run_fused",
     "agemm_run_bsp", "agemm_run_pull", "agemm_set_order", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
     "agemm_check",
     "agemm_last_error", "agemm_status_string",
@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.agemm_tiles.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_consumer_kernel.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_consumer_grid.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.agemm_mfma_plan.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_produce.argtypes = [vp, vp, ctypes.POINTER(Schedule), vp]
     lib.agemm_run_fused.argtypes = [vp, vp, vp, vp]
     lib.agemm_run_bsp.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Schedule), ctypes.c_int, vp]
@@ -71,6 +73,16 @@ def load() -> ctypes.CDLL:
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def mfma_plan(M: int, N: int, W: int, num_cus: int, tile_config: int = -1, split_mode: int = -1):
+    """Host-only plan of the MFMA consumer (agemm_mfma_plan): (tile config, grid, split)."""
+    cfg, grid, split = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = load().agemm_mfma_plan(int(M), int(N), int(W), int(num_cus), int(tile_config), int(split_mode),
+                                ctypes.byref(cfg), ctypes.byref(grid), ctypes.byref(split))
+    if rc != OK:
+        raise AgemmError(rc, f"agemm_mfma_plan: {status_string(rc)}")
+    return cfg.value, grid.value, bool(split.value)
 
 
 def status_string(code: int) -> str:

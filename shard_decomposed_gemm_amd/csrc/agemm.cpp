@@ -429,6 +429,18 @@ int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split) {
   return AGEMM_OK;
 }
 
+int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
+                    int32_t* grid, int32_t* split) {
+  if (M < 1 || N < 8 || W < 1 || W > kMaxShards || num_cus < 1 || tile_config < -1 ||
+      tile_config >= mfma_config_count() || split_mode < -1 || split_mode > 1)
+    return AGEMM_EINVAL;
+  const MfmaPlan p = mfma_plan(M, N, W, num_cus, tile_config, split_mode);
+  if (cfg) *cfg = p.cfg;
+  if (grid) *grid = (int32_t)p.grid;
+  if (split) *split = p.split ? 1 : 0;
+  return AGEMM_OK;
+}
+
 int agemm_set_order(agemm_ctx* ctx, int order) {
   if (!ctx) return AGEMM_EINVAL;
   if (order != AGEMM_ORDER_SHARD && order != AGEMM_ORDER_ARRIVAL) return fail(ctx, AGEMM_EINVAL, "unknown order %d", order);
