@@ -102,3 +102,7 @@ def test_null_context_is_rejected():
     assert lib.agemm_check(None) == agemm.EINVAL
     assert lib.agemm_destroy(None) == agemm.OK
     assert lib.agemm_last_error(None) == b"no context"
+    assert lib.agemm_set_order(None, 1) == agemm.EINVAL
+    g, sp = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.agemm_consumer_grid(None, ctypes.byref(g), ctypes.byref(sp)) == agemm.EINVAL
+    assert lib.agemm_consumer_kernel(None, None, None) == agemm.EINVAL
