@@ -155,3 +155,36 @@ def test_split_back_to_back_calls_reuse_counters(monkeypatch):
     ctx.check()
     assert not bad, bad
     ctx.close()
+
+
+def test_arrival_order_on_a_split_context_runs_whole_tiles(monkeypatch):
+    """A context that chose the split (10 tiles) asked for arrival order: those fused
+    calls run on whole tiles in arrival order, bit-exact against the oracle on exact
+    inputs, with tiles released out of order into a poisoned inbox; shard-order calls
+    on the same context still split."""
+    import torch
+    monkeypatch.delenv("AGEMM_SPLIT", raising=False)
+    W, M, K, N = 8, 300, 2048, 1032
+    a = gu.coarse_bits(0xF700 + M, M, K)
+    b = gu.coarse_bits(0xF800 + N, K, N)
+    sh = synth.shards(a, W)
+    ref = oracle.sharded_gemm(sh, b)
+    dsh = [gu.to_dev(s) for s in sh]
+    B = gu.to_dev(b)
+    ctx = _ctx(W, M, K, N, "f32")
+    assert ctx.split
+    nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
+    ctx.produce(nan)
+    ctx.produce(nan)
+    torch.cuda.synchronize()
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    for order in ("arrival", "shard", "arrival"):
+        ctx.set_order(order)
+        sched = synth.schedule(0xF900 + len(order), ctx.t, 10_000)
+        C = gu.empty_c(M, N, "f32")
+        ctx.produce(dsh, schedule=sched, stream=sp)
+        ctx.run_fused(B, C, stream=sc)
+        torch.cuda.synchronize()
+        ctx.check()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), order
+    ctx.close()
