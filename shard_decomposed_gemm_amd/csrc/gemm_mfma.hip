@@ -188,7 +188,10 @@ __device__ inline uint64_t load_coherent(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool GATED, bool OUTF32, bool SPLIT, bool ARRIVAL>
+// BNT: B is read by exactly one tile (one row block of C): its direct loads
+// are nontemporal (no L2 allocation).
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, bool GATED, bool OUTF32, bool SPLIT, bool ARRIVAL,
+          bool BNT = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   static_assert(!ARRIVAL || (GATED && !SPLIT), "arrival order is a mode of the gated whole-tile consumer");
   using S = Shape<BM, BN, BK, WM, WN>;
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     else
       __builtin_amdgcn_global_load_lds((const void*)(cb + b_off[j - S::A_ITERS]),
                                        (LDS_PTR(void))(dst + S::A_BYTES + ((j - S::A_ITERS) * NT + wave * 64) * 16),
-                                       16, 0, 0);
+                                       16, 0, BNT ? 2 : 0);
   };
 
   const uint32_t lds0 = lds_addr(smem);
@@ -764,6 +767,10 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
   // Arrival order needs a tile to span at least the prologue's steps (the
   // cursor publishes a tile's order at a barrier the prologue does not have).
   const bool arrival = arrival_requested(a) && !p.split && a.K / BK >= STAGES;
+  // One row block: every element of B is read by one tile only, so its loads
+  // skip L2 allocation (M = 128, N = 28672: 98.7 against 101.4 us). With more
+  // row blocks, tiles of one XCD share B panels through the L2.
+  const bool bnt = BM == 128 && BN == 128 && a.M <= BM && !p.split && !arrival;
 #define L4(G_, F_, S_, A_)                                                                                     \
   do {                                                                                                        \
     if (t.start)                                                                                              \
@@ -773,11 +780,27 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
       hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, S_, A_>), grid, block, 0, s, a); \
   } while (0)
 #define L(G_, F_, S_) L4(G_, F_, S_, false)
+#define L5(G_, F_)                                                                                              \
+  do {                                                                                                         \
+    if (t.start)                                                                                               \
+      hipExtLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, false, false, true>), grid,  \
+                            block, 0, s, t.start, t.stop, 0, a);                                               \
+    else                                                                                                       \
+      hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, STAGES, WM, WN, G_, F_, false, false, true>), grid,     \
+                         block, 0, s, a);                                                                      \
+  } while (0)
 #define L2(S_)                                                     \
   do {                                                             \
     if (gated) { if (out_f32) L(true, true, S_); else L(true, false, S_); }   \
     else { if (out_f32) L(false, true, S_); else L(false, false, S_); }       \
   } while (0)
+  if constexpr (BM == 128 && BN == 128) {
+    if (bnt) {
+      if (gated) { if (out_f32) L5(true, true); else L5(true, false); }
+      else { if (out_f32) L5(false, true); else L5(false, false); }
+      return hipGetLastError();
+    }
+  }
   if (arrival) {
     if (out_f32) L4(true, true, false, true);
     else L4(true, false, false, true);
@@ -789,6 +812,7 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
 #undef L2
 #undef L
 #undef L4
+#undef L5
   return hipGetLastError();
 }
 
