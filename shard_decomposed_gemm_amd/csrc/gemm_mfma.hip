@@ -768,9 +768,11 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
   // cursor publishes a tile's order at a barrier the prologue does not have).
   const bool arrival = arrival_requested(a) && !p.split && a.K / BK >= STAGES;
   // One row block: every element of B is read by one tile only, so its loads
-  // skip L2 allocation (M = 128, N = 28672: 98.7 against 101.4 us). With more
-  // row blocks, tiles of one XCD share B panels through the L2.
-  const bool bnt = BM == 128 && BN == 128 && a.M <= BM && !p.split && !arrival;
+  // skip L2 allocation (M = 128, N = 28672, 224 workgroups: 98.7 against
+  // 101.4 us). With more row blocks, tiles of one XCD share B panels through
+  // the L2; with few workgroups the nontemporal loads streamed slower (32
+  // tiles: 73 against 48 us), so at least half of the CUs must be busy.
+  const bool bnt = BM == 128 && BN == 128 && a.M <= BM && !p.split && !arrival && 2 * p.grid >= a.num_cus;
 #define L4(G_, F_, S_, A_)                                                                                     \
   do {                                                                                                        \
     if (t.start)                                                                                              \
