@@ -123,18 +123,23 @@ def test_timeout_reports_and_recovers(M):
     order = np.arange(ctx.t, dtype=np.int32)
     offs = np.zeros(ctx.t, dtype=np.int64)
     offs[-1] = 30_000_000  # last tile 30 ms late
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
-    C = gu.empty_c(M, N, "f32")
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ctx.produce(dsh, schedule=(order, offs), stream=sp)
-    t0.record(sc)
-    ctx.run_fused(B, C, stream=sc)
-    t1.record(sc)
-    torch.cuda.synchronize()
-    if t0.elapsed_time(t1) < 1.0:
-        # HIP mapped both streams onto one hardware queue: the consumer ran after the
-        # producer had released every tile, so there was nothing to time out on.
+    sp = torch.cuda.Stream()
+    for _ in range(4):
+        # HIP maps streams onto a few hardware queues; when the consumer's stream
+        # shares the producer's queue, the consumer runs after every tile is out and
+        # there is nothing to time out on (a correct run): then try a fresh stream.
+        sc = torch.cuda.Stream()
+        C = gu.empty_c(M, N, "f32")
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ctx.produce(dsh, schedule=(order, offs), stream=sp)
+        t0.record(sc)
+        ctx.run_fused(B, C, stream=sc)
+        t1.record(sc)
+        torch.cuda.synchronize()
+        if t0.elapsed_time(t1) >= 1.0:
+            break
         ctx.check()
+    else:
         pytest.skip("producer and consumer streams shared a hardware queue (no overlap)")
     with pytest.raises(AgemmError) as ei:
         ctx.check()
