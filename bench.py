@@ -55,6 +55,31 @@ KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "agemm_internal.h"), "small_m": ("ge
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "consumer_hbm_traffic.md")
 
 
+def device_peaks(measure: bool) -> dict:
+    """The peaks the rooflines use (published), the same derived from the device
+    properties, and the device's measured ceilings (register-only fp16 MFMA loop,
+    streaming read of 2 GiB, beyond the 256 MB last-level cache) as secondary
+    references."""
+    import torch
+    from shard_decomposed_gemm_amd import agemm
+    info = agemm.device_info()
+    derived = {
+        # CDNA4: 4096 dense fp16 FLOP per clock per CU. HBM3E: 4 bits per pin per
+        # reported memory clock (8 Gb/s per pin at the 2 GHz the properties give).
+        "fp16_tflops": info["cus"] * 4096 * info["clock_khz"] * 1e3 / 1e12,
+        "hbm_gbs": 4.0 * info["mem_clock_khz"] * 1e3 * info["bus_bits"] / 8 / 1e9,
+    }
+    out = {"published": {"fp16_tflops": PEAK_FP16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
+           "device_props": dict(info, **{k + "_from_props": v for k, v in derived.items()})}
+    if measure:
+        buf = torch.zeros(2 << 30, dtype=torch.uint8, device="cuda")
+        out["measured"] = {"mfma_f16_register_loop_tflops": agemm.probe_mfma(100, 30),
+                           "stream_read_gbs": agemm.probe_read(buf, 10, 20), "read_bytes": buf.numel()}
+        del buf
+        torch.cuda.synchronize()
+    return out
+
+
 def kernel_digest(kind: str) -> str:
     """Digest of the consumer kernel's sources: counter figures taken from another
     version of the kernel are not reported."""
@@ -267,6 +292,8 @@ def main():
                     help="flag-tile order of the fused consumer (agemm_set_order)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured ceilings (fp16 MFMA register loop, streaming read)")
     ap.add_argument("--one-stream", action="store_true",
                     help="producer and consumer on one stream (the consumer then finds every flag up); "
                          "for counter collection, which serialises kernel dispatches")
@@ -396,6 +423,14 @@ def main():
                   "fused_speedup_vs_bsp": bsp_sync / fused}
         print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
 
+    peaks = device_peaks(not args.no_peaks)
+    if "measured" in peaks:
+        m = peaks["measured"]
+        ceil = m["mfma_f16_register_loop_tflops"] if roof["bound"] == "mfma" else m["stream_read_gbs"]
+        roof["frac_of_measured_ceiling"] = roof["achieved"] / ceil
+        print(f"[bench] measured ceilings: {m['mfma_f16_register_loop_tflops']:.0f} TFLOP/s fp16 MFMA loop, "
+              f"{m['stream_read_gbs']:.0f} GB/s streaming read", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(W, M, K, N, args.cpu_budget)
@@ -423,6 +458,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "ladder": ladder,
+        "peaks": peaks,
     }
     print(json.dumps(line), flush=True)
     ctx.close()

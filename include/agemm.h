@@ -200,6 +200,37 @@ int agemm_set_spin_timeout_us(agemm_ctx* ctx, int64_t us);
 int agemm_timing_begin(agemm_ctx* ctx, int32_t max_launches);
 int agemm_timing_end(agemm_ctx* ctx, float* us, int32_t max, int32_t* count);
 
+/* Ceilings of the current device, secondary references beside the published
+ * peaks the rooflines are quoted against (the measurement of the AG+GEMM
+ * analysis page's roofline discussion: compute-bound at large M, B streaming
+ * at M = 1). No context needed; calibration calls, not hot-path ones.
+ *
+ * agemm_device_info: compute units, shader clock and memory clock in kHz and
+ * memory bus width in bits, as the HIP device properties report them.
+ * EINVAL for a NULL output, EHIP if the runtime cannot answer.
+ *
+ * agemm_probe_mfma: dense fp16 MFMA throughput from registers only
+ * (v_mfma_f32_32x32x16_f16, four independent accumulators per wave, two
+ * workgroups of four waves per CU, no memory traffic). Runs `warmup` launches,
+ * then times `launches` back-to-back launches (about 1.8 ms each at 2.5 PF)
+ * with HIP events on `stream` and waits for them; *tflops = 2 x
+ * multiply-adds / average launch time. `out` is a caller-owned device buffer
+ * of at least 65536 bytes, 4-byte aligned, that receives one word per
+ * workgroup (contents meaningless). EINVAL for NULL pointers, warmup < 0 or
+ * launches < 1; EHIP on a runtime failure.
+ *
+ * agemm_probe_read: streaming read of the caller's device buffer `buf`
+ * (`bytes` >= 16, a multiple of 16, 16-byte aligned; make it larger than the
+ * 256 MB last-level cache so that HBM serves it) with 16-byte nontemporal
+ * loads, eight in flight per thread, eight workgroups per CU, each reading
+ * one contiguous chunk. Same timing and
+ * `out` contract as agemm_probe_mfma; *gbs = bytes / average launch time,
+ * in GB/s (1e9 bytes). The buffer is only read. */
+int agemm_device_info(int32_t* cus, int32_t* clock_khz, int32_t* mem_clock_khz, int32_t* bus_bits);
+int agemm_probe_mfma(int32_t warmup, int32_t launches, void* out, void* stream, double* tflops);
+int agemm_probe_read(const void* buf, int64_t bytes, int32_t warmup, int32_t launches, void* out, void* stream,
+                     double* gbs);
+
 /* After the caller has synchronised: AGEMM_ETIMEOUT if a consumer timed out
  * since the last check (the error word is then cleared), else AGEMM_OK. */
 int agemm_check(agemm_ctx* ctx);

@@ -21,7 +21,7 @@ F16, F32 = 0, 1
 EXPORTED = (
     "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_mfma_plan", "agemm_produce", "agemm_run_fused",
     "agemm_run_bsp", "agemm_run_pull", "agemm_set_order", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
-    "agemm_check",
+    "agemm_check", "agemm_device_info", "agemm_probe_mfma", "agemm_probe_read",
     "agemm_last_error", "agemm_status_string",
 )
 
@@ -64,6 +64,9 @@ def load() -> ctypes.CDLL:
     lib.agemm_timing_begin.argtypes = [vp, i32]
     lib.agemm_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
     lib.agemm_check.argtypes = [vp]
+    lib.agemm_device_info.argtypes = [ctypes.POINTER(i32)] * 4
+    lib.agemm_probe_mfma.argtypes = [i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
+    lib.agemm_probe_read.argtypes = [vp, i64, i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
     lib.agemm_last_error.argtypes = [vp]
     lib.agemm_last_error.restype = ctypes.c_char_p
     lib.agemm_status_string.argtypes = [ctypes.c_int]
@@ -87,6 +90,39 @@ def mfma_plan(M: int, N: int, W: int, num_cus: int, tile_config: int = -1, split
 
 def status_string(code: int) -> str:
     return load().agemm_status_string(code).decode()
+
+
+def device_info() -> dict:
+    """agemm_device_info: compute units, clocks (kHz) and memory bus width (bits)."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    rc = load().agemm_device_info(*[ctypes.byref(x) for x in v])
+    if rc != OK:
+        raise AgemmError(rc, f"agemm_device_info: {status_string(rc)}")
+    return dict(zip(("cus", "clock_khz", "mem_clock_khz", "bus_bits"), (x.value for x in v)))
+
+
+def probe_mfma(warmup: int = 100, launches: int = 30, stream=None) -> float:
+    """agemm_probe_mfma: register-only fp16 MFMA throughput of the device, TFLOP/s."""
+    import torch
+    out = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    v = ctypes.c_double()
+    rc = load().agemm_probe_mfma(int(warmup), int(launches), out.data_ptr(), _stream_handle(stream), ctypes.byref(v))
+    if rc != OK:
+        raise AgemmError(rc, f"agemm_probe_mfma: {status_string(rc)}")
+    return v.value
+
+
+def probe_read(buf, warmup: int = 10, launches: int = 20, stream=None) -> float:
+    """agemm_probe_read over the bytes of a contiguous device tensor: streaming read, GB/s."""
+    import torch
+    out = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    nbytes = buf.numel() * buf.element_size()
+    v = ctypes.c_double()
+    rc = load().agemm_probe_read(_ptr(buf, "buf"), ctypes.c_int64(nbytes), int(warmup), int(launches),
+                                 out.data_ptr(), _stream_handle(stream), ctypes.byref(v))
+    if rc != OK:
+        raise AgemmError(rc, f"agemm_probe_read: {status_string(rc)}")
+    return v.value
 
 
 def _stream_handle(stream) -> int | None:

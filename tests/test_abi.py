@@ -106,3 +106,19 @@ def test_null_context_is_rejected():
     g, sp = ctypes.c_int32(), ctypes.c_int32()
     assert lib.agemm_consumer_grid(None, ctypes.byref(g), ctypes.byref(sp)) == agemm.EINVAL
     assert lib.agemm_consumer_kernel(None, None, None) == agemm.EINVAL
+
+
+def test_probes_reject_bad_arguments_without_gpu():
+    """The calibration probes validate their arguments before any HIP call."""
+    lib = agemm.load()
+    v = ctypes.c_double()
+    i = ctypes.c_int32()
+    assert lib.agemm_device_info(None, ctypes.byref(i), ctypes.byref(i), ctypes.byref(i)) == agemm.EINVAL
+    assert lib.agemm_probe_mfma(1, 1, None, None, ctypes.byref(v)) == agemm.EINVAL      # no out buffer
+    assert lib.agemm_probe_mfma(-1, 1, 64, None, ctypes.byref(v)) == agemm.EINVAL       # warmup < 0
+    assert lib.agemm_probe_mfma(0, 0, 64, None, ctypes.byref(v)) == agemm.EINVAL        # no timed launch
+    assert lib.agemm_probe_mfma(0, 1, 64, None, None) == agemm.EINVAL                   # no result pointer
+    assert lib.agemm_probe_read(64, 15, 0, 1, 64, None, ctypes.byref(v)) == agemm.EINVAL  # not a multiple of 16
+    assert lib.agemm_probe_read(72, 64, 0, 1, 64, None, ctypes.byref(v)) == agemm.EINVAL  # misaligned buffer
+    assert lib.agemm_probe_read(None, 64, 0, 1, 64, None, ctypes.byref(v)) == agemm.EINVAL
+    assert lib.agemm_probe_read(64, 64, 0, 1, 66, None, ctypes.byref(v)) == agemm.EINVAL  # misaligned out
