@@ -1,7 +1,9 @@
 """Full-size workloads (K = 8192, N = 28672, W = 8) in the launch configuration the
 benchmark times: sampled entries against the oracle, and every entry compared
 across the fused, bulk-synchronous and pull paths (same kernels, same summation
-order, so the three must agree bit for bit).
+order, so the three must agree bit for bit; in arrival order the fused consumer
+sums the shards in the order their tiles came up, so it is held to the oracle's
+tolerance against the other two instead).
 """
 import numpy as np
 import pytest
@@ -14,11 +16,14 @@ pytestmark = pytest.mark.gpu
 
 W, K, N = 8, 8192, 28672
 CONFIGS = {
-    # name: (M, schedule?)
-    "decode_m1": (1, False),
-    "xover_m128": (128, False),
-    "prefill_m4096": (4096, False),
-    "ooo_m512": (512, True),
+    # name: (M, schedule?, flag-tile order of the fused consumer)
+    "decode_m1": (1, False, "shard"),
+    "xover_m128": (128, False, "shard"),
+    "prefill_m4096": (4096, False, "shard"),
+    "ooo_m512": (512, True, "shard"),
+    # the benchmark's --order arrival runs of the two MFMA-bound workloads
+    "ooo_m512_arrival": (512, True, "arrival"),
+    "prefill_m4096_arrival": (4096, False, "arrival"),
 }
 
 
@@ -32,12 +37,13 @@ def weight():
 def test_full_size(name, weight):
     import torch
     from shard_decomposed_gemm_amd import Context
-    M, scheduled = CONFIGS[name]
+    M, scheduled, order = CONFIGS[name]
     b, B = weight
     a = synth.matrix_f16(0xA100 + M, M, K)
     sh = synth.shards(a, W)
     dsh = [gu.to_dev(s) for s in sh]
     ctx = Context(W, M, K, N, c_dtype="f16")
+    ctx.set_order(order)
     sched = synth.schedule(0x5005, ctx.t, 20_000) if scheduled else None
     sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
     Cf = gu.empty_c(M, N, "f16")
@@ -51,8 +57,12 @@ def test_full_size(name, weight):
     ctx.run_pull(dsh, B, Cp)
     torch.cuda.synchronize()
     ctx.check()
-    assert torch.equal(Cf.view(torch.int16), Cb.view(torch.int16))
-    assert torch.equal(Cf.view(torch.int16), Cp.view(torch.int16))
+    assert torch.equal(Cb.view(torch.int16), Cp.view(torch.int16))
+    if order == "shard":
+        assert torch.equal(Cf.view(torch.int16), Cb.view(torch.int16))
+    else:
+        diff = (Cf.float() - Cb.float()).abs().max().item()
+        assert diff <= oracle.tolerance(K), diff
     got = Cf.float().cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
     rng = np.random.default_rng(M)
