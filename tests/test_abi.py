@@ -122,3 +122,34 @@ def test_probes_reject_bad_arguments_without_gpu():
     assert lib.agemm_probe_read(72, 64, 0, 1, 64, None, ctypes.byref(v)) == agemm.EINVAL  # misaligned buffer
     assert lib.agemm_probe_read(None, 64, 0, 1, 64, None, ctypes.byref(v)) == agemm.EINVAL
     assert lib.agemm_probe_read(64, 64, 0, 1, 66, None, ctypes.byref(v)) == agemm.EINVAL  # misaligned out
+
+
+def test_plain_c_program_links_and_calls_the_library(tmp_path):
+    """The boundary is a C ABI: a C99 program that includes both headers links against
+    libagemm.so and calls host-only entry points (no GPU needed): the work plan of the
+    prefill workload, a status name, and a shape error from agemm_create."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    lib = agemm.load()._name
+    libdir = os.path.dirname(lib)
+    src = tmp_path / "main.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"agemm.h\"\n#include \"fdcombine.h\"\n"
+        "int main(void) {\n"
+        "  int32_t cfg = -9, grid = -9, split = -9;\n"
+        "  int rc = agemm_mfma_plan(4096, 28672, 8, 256, -1, -1, &cfg, &grid, &split);\n"
+        "  printf(\"%s %d %d %d\\n\", agemm_status_string(rc), cfg, grid, split);\n"
+        "  agemm_ctx* ctx = 0;\n"
+        "  printf(\"%s\\n\", agemm_status_string(agemm_create(&ctx, 8, 4, 8192 + 8, 256, AGEMM_F16, 0)));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "main"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-L", libdir, "-lagemm", "-Wl,-rpath," + libdir,
+                        "-Wl,-rpath-link,/opt/rocm/lib", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split("\n")[:2] == ["AGEMM_OK 0 256 0", "AGEMM_ESHAPE"]
