@@ -158,7 +158,11 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
 
 /* Flag-gated consumer: C = sum_s Inbox(s) . B_s, waiting on Flags(s, kt)
  * before reading each k-tile. Meant to run concurrently with agemm_produce
- * on another stream. B: K x N fp16; C: M x N in the context's dtype. */
+ * on another stream. B: K x N fp16; C: M x N in the context's dtype.
+ * HIP maps streams onto a few hardware queues (4 by default); two streams
+ * on one queue run their work in submission order, so the consumer then
+ * starts only after the whole producer (still correct, no overlap). Streams
+ * created one after the other land on different queues. */
 int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream);
 
 /* Bulk-synchronous baseline on the same GPU: a gather kernel copies the
