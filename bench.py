@@ -245,6 +245,9 @@ def run_fd(args):
         ladder = {"bsp_host_sync_us": bsp_sync, "bsp_device_dep_us": bsp_dev, "fused_us": fused,
                   "consumer_only_us": alone, "fused_speedup_vs_bsp": bsp_sync / fused}
         print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
+    peaks = device_peaks(not args.no_peaks)
+    if "measured" in peaks:
+        roof["frac_of_measured_ceiling"] = roof["achieved"] / peaks["measured"]["stream_read_gbs"]
     cpu = None if args.no_cpu else fd_cpu_baseline(W, H, D, min(args.cpu_budget, 10.0))
     line = {
         "metric": "Flash-Decode combine step latency (producer of W partials || flag-gated combine)",
@@ -255,7 +258,7 @@ def run_fd(args):
         "config": {"workload": args.workload, "W": W, "H": H, "D": D, "heads_per_tile": HT, "out_dtype": odt,
                    "tiles": ctx.t, "schedule": f"seeded permutation, cumulative U[0,{max_delay // 1000}] us delays",
                    "release_span_us": float(sched[1][-1]) / 1e3},
-        "roofline": roof, "cpu_baseline": cpu, "ladder": ladder,
+        "roofline": roof, "cpu_baseline": cpu, "ladder": ladder, "peaks": peaks,
     }
     print(json.dumps(line), flush=True)
     ctx.close()
