@@ -50,7 +50,7 @@ PEAK_HBM_GBS = 8000.0
 
 
 CSRC = os.path.join(ROOT, "shard_decomposed_gemm_amd", "csrc")
-KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "agemm_internal.h"), "small_m": ("gemm_small_m.hip", "agemm_internal.h"),
+KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "mfma_sched.h", "agemm_internal.h"), "small_m": ("gemm_small_m.hip", "agemm_internal.h"),
                   "fd": ("fd_combine.hip", "fd_internal.h", "agemm_internal.h")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "consumer_hbm_traffic.md")
 
@@ -114,28 +114,43 @@ def algorithmic(W, M, K, N, c_bytes):
     return flops, consumer_bytes, path_bytes
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(W, M, K, N, budget_s: float):
-    """The oracle as it stands, on a bounded row sample of the same workload."""
-    import numpy as np
+    """The oracle as it stands, on a bounded row sample of the same workload. The oracle
+    splits rows over its threads, so the sample is a multiple of the thread count (one
+    row per thread at M = 1 is all there is)."""
     import oracle
     import synth
     threads = oracle.default_threads()
     b = synth.matrix_f16(0xB002, K, N)
-    # rows per second of the oracle: measure one row first, then size the sample
-    rows = 1
-    a = synth.matrix_f16(0xA102, max(M, 1), K)
+    a = synth.matrix_f16(0xA100 + M, M, K)
+    # one row per thread first (this includes the oracle's own fp16 decode of B), then a
+    # sample sized to the budget
+    rows = min(M, threads)
     t0 = time.perf_counter()
     oracle.sharded_gemm(synth.shards(a[:rows], W), b, nthreads=threads)
     t1 = time.perf_counter() - t0
-    rows = int(max(1, min(M, threads * max(1, int(budget_s / max(t1, 1e-6) / threads)))))
-    rows = min(rows, M)
-    if rows > 1:
+    if t1 < budget_s / 2 and rows < M:
+        rows = min(M, rows * max(1, int(budget_s / t1)))
         t0 = time.perf_counter()
         oracle.sharded_gemm(synth.shards(a[:rows], W), b, nthreads=threads)
         t1 = time.perf_counter() - t0
     flops = 2.0 * rows * K * N
-    return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": min(threads, rows),
-            "kind": "oracle", "sample": f"{rows} of {M} rows at full K={K}, N={N}, W={W} (binary64, {t1:.2f} s)",
+    cores = min(threads, rows)
+    return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"{rows} of {M} rows at full K={K}, N={N}, W={W} (binary64, {cores} threads, {t1:.2f} s, "
+                      f"including the oracle's decode of B)",
             "seconds": t1}
 
 
@@ -264,6 +279,80 @@ def run_fd(args):
     ctx.close()
 
 
+def run_sweep(args):
+    """The fused-vs-BSP ladder across M at the sweep shape of the analysis page's
+    AG+GEMM experiments (W = 8, K = 8192, N = 28672, M varied), fp16 C, shard order."""
+    import numpy as np
+    import torch
+    import synth
+    from shard_decomposed_gemm_amd import Context
+
+    Ms = [int(x) for x in args.sweep.split(",") if x.strip()]
+    W, K, N = W_DEF, K_DEF, N_DEF
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).to(dev)
+    B0 = to_dev(synth.matrix_f16(0xB002, K, N))
+    Bs = [B0, B0.clone()]
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    rows = []
+
+    def timeit(fn, n):
+        for i in range(max(3, n // 5)):
+            fn(i)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e6 / n
+
+    for M in Ms:
+        print(f"[sweep] M={M}", file=sys.stderr, flush=True)
+        shards = [to_dev(x) for x in synth.shards(synth.matrix_f16(0xA100 + M, M, K), W)]
+        Cs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(2)]
+        ctx = Context(W, M, K, N, c_dtype="f16")
+
+        def fused_step(i):
+            ctx.produce(shards, stream=sp)
+            ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc)
+
+        prewarm(fused_step, args.prewarm_ms)
+        n = args.steps
+        r = {"M": M, "consumer": ctx.consumer_info()}
+        # fused and the BSP variants interleaved twice, so a clock drift hits them alike
+        for rep in range(2):
+            r.setdefault("fused_us", []).append(timeit(fused_step, n))
+            r.setdefault("bsp_host_sync_us", []).append(timeit(
+                lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], host_sync=True, stream=sc), n))
+            r.setdefault("bsp_device_dep_us", []).append(timeit(
+                lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], host_sync=False, stream=sc), n))
+            r.setdefault("pull_us", []).append(timeit(
+                lambda i: ctx.run_pull(shards, Bs[i & 1], Cs[i & 1], stream=sc), n))
+        ctx.produce(shards)
+        torch.cuda.synchronize()
+        r["consumer_only_us"] = [timeit(lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), n)]
+        ctx.check()
+        for k in list(r):
+            if k.endswith("_us"):
+                r[k] = float(min(r[k]))
+        r["tflops_fused"] = 2.0 * M * K * N / (r["fused_us"] * 1e-6) / 1e12
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        ctx.close()
+        del shards, Cs
+    print("\n| M | consumer | fused | BSP host sync | BSP device dep | Pull | consumer alone | fused vs BSP "
+          "(host / device) |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        c = r["consumer"]
+        kern = ("small-M" if c["kind"] == "small_m" else
+                f"cfg {c['tile_config']}, {c['tiles']} tiles / {c['grid']} WG" + (", split" if c["split"] else ""))
+        print(f"| {r['M']} | {kern} | {r['fused_us']:.1f} | {r['bsp_host_sync_us']:.1f} | "
+              f"{r['bsp_device_dep_us']:.1f} | {r['pull_us']:.1f} | {r['consumer_only_us']:.1f} | "
+              f"{r['bsp_host_sync_us'] / r['fused_us']:.3f}x / {r['bsp_device_dep_us'] / r['fused_us']:.3f}x |")
+
+
 def calibrate_copy(steps: int):
     """A plain device-to-device copy of 1 GiB: the known byte count (1 GiB read, 1 GiB
     written per dispatch) against which FETCH_SIZE / WRITE_SIZE are scaled."""
@@ -287,7 +376,10 @@ def main():
     # the pages' methodology: 500 timed iterations after 100 warmup iterations
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode_m1", choices=list(WORKLOADS) + list(FD_WORKLOADS))
+    ap.add_argument("--workload", default="prefill_m4096", choices=list(WORKLOADS) + list(FD_WORKLOADS))
+    ap.add_argument("--sweep", default=None,
+                    help="comma-separated M values at K=8192, N=28672, W=8: the fused / BSP / Pull ladder "
+                         "per M (one JSON object per M, then a markdown table); no headline line")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps, so the engine clock has settled")
@@ -312,6 +404,8 @@ def main():
 
     if args.workload in FD_WORKLOADS:
         return run_fd(args)
+    if args.sweep:
+        return run_sweep(args)
 
     import numpy as np
     import torch
@@ -416,14 +510,17 @@ def main():
         bsp_dev = timeit(lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched, host_sync=False,
                                                stream=sc), n)
         fused = timeit(fused_step, n)
+        ctx.set_strict_acquire(True)
+        fused_strict = timeit(fused_step, n)
+        ctx.set_strict_acquire(False)
         ctx.produce(shards)
         torch.cuda.synchronize()
         consumer_only = timeit(lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), n)
         pull = timeit(lambda i: ctx.run_pull(shards, Bs[i & 1], Cs[i & 1], stream=sc), n)
         ctx.check()
         ladder = {"bsp_host_sync_us": bsp_sync, "bsp_device_dep_us": bsp_dev, "fused_us": fused,
-                  "consumer_only_us": consumer_only, "pull_us": pull,
-                  "fused_speedup_vs_bsp": bsp_sync / fused}
+                  "fused_strict_acquire_us": fused_strict, "consumer_only_us": consumer_only, "pull_us": pull,
+                  "fused_speedup_vs_bsp": bsp_sync / fused, "fused_speedup_vs_bsp_device_dep": bsp_dev / fused}
         print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
 
     peaks = device_peaks(not args.no_peaks)

@@ -141,6 +141,26 @@ int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_con
 int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
                     int32_t* grid, int32_t* split);
 
+/* Everything the context's consumer launches are built from (fixed at create
+ * time, except where the order set by agemm_set_order changes it, as noted).
+ *   kind           0: MFMA tile kernel, 1: small-M split-K streaming kernel
+ *   tile_config    MFMA tile configuration 0..3 (-1 for small-M)
+ *   block_m/_n     output tile of one MFMA workgroup (0 for small-M)
+ *   tiles          output tiles (MFMA) or work items (small-M: K-ranges x column blocks)
+ *   grid           workgroups of the launch (a persistent grid: at most one MFMA
+ *                  workgroup, or two small-M workgroups, per compute unit)
+ *   split          1: the stream-K split over (output tile, shard) units
+ *   b_nontemporal  1: B's loads skip L2 allocation (one row block of whole tiles;
+ *                  not in arrival order)
+ *   tiles_per_wg   most output tiles one workgroup runs (whole tiles), 1 with the split
+ *   ranges         small-M K-ranges (0 for MFMA) */
+typedef struct {
+  int32_t kind, tile_config, block_m, block_n;
+  int32_t tiles, grid, split, b_nontemporal;
+  int32_t tiles_per_wg, ranges;
+} agemm_consumer_desc;
+int agemm_consumer_info(const agemm_ctx* ctx, agemm_consumer_desc* out);
+
 /* Launch shape of the MFMA consumer: *grid = its workgroups, *split = 1 when
  * it runs the stream-K split described above, else 0. For the small-M kernel
  * *grid = -1 and *split = 0. Either output pointer may be NULL. */
@@ -187,6 +207,15 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
  * and on the MFMA consumer only; the small-M consumer keeps every K-range
  * resident at once and needs no reordering. EINVAL for an unknown order. */
 int agemm_set_order(agemm_ctx* ctx, int order);
+
+/* Flag-wait mode of later run_fused calls: 0 = the consumer reads a tile's
+ * data after seeing its flag with no fence (no line of the tile was read in
+ * the launch before, so no cache holds a stale copy; loads follow the flag by
+ * control dependency), 1 = an agent-scope acquire fence after every wait (and
+ * after the launch's first look at the flags). Default: the
+ * AGEMM_STRICT_ACQUIRE environment variable at create time, else 0. EINVAL
+ * for other values. */
+int agemm_set_strict_acquire(agemm_ctx* ctx, int strict);
 
 /* Sets the consumer's spin timeout in microseconds (default 2,000,000, or
  * the AGEMM_SPIN_TIMEOUT_MS environment variable at create time). */

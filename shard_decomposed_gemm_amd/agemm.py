@@ -21,6 +21,7 @@ F16, F32 = 0, 1
 EXPORTED = (
     "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_mfma_plan", "agemm_produce", "agemm_run_fused",
     "agemm_run_bsp", "agemm_run_pull", "agemm_set_order", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
+    "agemm_consumer_info", "agemm_set_strict_acquire",
     "agemm_check", "agemm_device_info", "agemm_probe_mfma", "agemm_probe_read",
     "agemm_last_error", "agemm_status_string",
 )
@@ -34,6 +35,12 @@ class AgemmError(RuntimeError):
 
 class Schedule(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("order", ctypes.c_void_p), ("offset_ns", ctypes.c_void_p)]
+
+
+class ConsumerDesc(ctypes.Structure):
+    """agemm_consumer_desc: the consumer launch a context's calls make."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("kind", "tile_config", "block_m", "block_n", "tiles", "grid", "split",
+                                               "b_nontemporal", "tiles_per_wg", "ranges")]
 
 
 _lib = None
@@ -60,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.agemm_run_bsp.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Schedule), ctypes.c_int, vp]
     lib.agemm_run_pull.argtypes = [vp, vp, vp, vp, vp]
     lib.agemm_set_order.argtypes = [vp, ctypes.c_int]
+    lib.agemm_consumer_info.argtypes = [vp, ctypes.POINTER(ConsumerDesc)]
+    lib.agemm_set_strict_acquire.argtypes = [vp, ctypes.c_int]
     lib.agemm_set_spin_timeout_us.argtypes = [vp, i64]
     lib.agemm_timing_begin.argtypes = [vp, i32]
     lib.agemm_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
@@ -237,6 +246,18 @@ class Context:
         if code is None:
             raise ValueError("order must be 'shard' or 'arrival'")
         self._raise(self._lib.agemm_set_order(self._h, code), "agemm_set_order")
+
+    def consumer_info(self) -> dict:
+        """agemm_consumer_info: the consumer launch of this context's calls (under its current order)."""
+        d = ConsumerDesc()
+        self._raise(self._lib.agemm_consumer_info(self._h, ctypes.byref(d)), "agemm_consumer_info")
+        out = {name: getattr(d, name) for name, _ in ConsumerDesc._fields_}
+        out["kind"] = "small_m" if d.kind == 1 else "mfma"
+        return out
+
+    def set_strict_acquire(self, strict: bool):
+        """Flag-wait mode of later run_fused calls: False = no fence, True = agent-scope acquire."""
+        self._raise(self._lib.agemm_set_strict_acquire(self._h, 1 if strict else 0), "agemm_set_strict_acquire")
 
     def set_spin_timeout_us(self, us: int):
         self._raise(self._lib.agemm_set_spin_timeout_us(self._h, int(us)), "agemm_set_spin_timeout_us")

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "agemm_internal.h"
+#include "host_common.h"
 
 using namespace agemm;
 
@@ -51,37 +52,20 @@ struct agemm_ctx {
   ErrWord* err_dev = nullptr;
 
   int32_t rows_per_item = 1, items_per_tile = 1;
+  int32_t producer_wgs = 0;      // persistent grid of the push producer (0: one workgroup per item)
   uint32_t epoch = 0;            // produce calls so far; epoch e uses inbox e & 1
   uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox so far
   uint32_t parity_fused = 0, parity_bsp = 0;
 
-  // Ordering between calls on different streams. One event is recorded per
-  // call; a wait is skipped when the event was recorded on the waiting
-  // stream (in-stream order already holds, and every dependency packet costs
-  // command-processor time between kernels).
-  hipEvent_t ev_consumer = nullptr;  // after the last BSP or pull consumer call
-  hipEvent_t ev_producer = nullptr;  // after the last produce call
-  hipEvent_t ev_fused[2] = {nullptr, nullptr};  // after the last fused consumer of each inbox
-  hipEvent_t last_consumer_ev = nullptr;        // the event of the last consumer call, whichever
-  hipStream_t consumer_stream = nullptr, producer_stream = nullptr, fused_stream[2] = {nullptr, nullptr};
-  bool consumer_pending = false, producer_pending = false;
-  bool fused_pending[2] = {false, false};
-  bool consumed_this_epoch = false;
-
-  // Kernel timing (agemm_timing_begin/end): events attached to the dispatch
-  // of each consumer kernel launched while active, up to timing_cap launches.
-  std::vector<hipEvent_t> timing_events;  // start, stop pairs
-  int32_t timing_cap = 0, timing_count = 0;
-  bool timing_on = false;
+  StreamOrder so;      // ordering between calls on different streams
+  KernelTimer timer;   // agemm_timing_begin/end
 
   std::string last_error;
 };
 
 namespace {
 
-const char* kStatusNames[] = {"AGEMM_OK",  "AGEMM_EINVAL",   "AGEMM_ESHAPE", "AGEMM_ENOMEM",
-                              "AGEMM_EHIP", "AGEMM_ETIMEOUT", "AGEMM_ESTATE"};
-
+int fail(agemm_ctx* c, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
 int fail(agemm_ctx* c, int code, const char* fmt, ...) {
   if (c) {
     char buf[512];
@@ -89,16 +73,12 @@ int fail(agemm_ctx* c, int code, const char* fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    c->last_error = std::string(kStatusNames[code]) + ": " + buf;
+    set_error(&c->last_error, code, "%s", buf);
   }
   return code;
 }
 
-int hip_fail(agemm_ctx* c, hipError_t e, const char* what) {
-  return fail(c, AGEMM_EHIP, "%s: %s", what, hipGetErrorString(e));
-}
-
-bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int hip_fail(agemm_ctx* c, hipError_t e, const char* what) { return set_hip_error(&c->last_error, e, what); }
 
 int check_shards(agemm_ctx* c, const void* const* a_shards) {
   if (!a_shards) return fail(c, AGEMM_EINVAL, "a_shards is NULL");
@@ -107,32 +87,8 @@ int check_shards(agemm_ctx* c, const void* const* a_shards) {
   return AGEMM_OK;
 }
 
-// Validates a schedule and converts it into the producer's arguments.
 int fill_schedule(agemm_ctx* c, const agemm_schedule* sched, ProduceArgs& pa) {
-  pa.has_delay = 0;
-  for (int p = 0; p < c->t; ++p) {
-    pa.order[p] = p;
-    pa.offset_ticks[p] = 0;
-  }
-  if (!sched) return AGEMM_OK;
-  if (sched->n != c->t || !sched->order || !sched->offset_ns)
-    return fail(c, AGEMM_EINVAL, "schedule must have n == T (%d) entries and non-NULL arrays", c->t);
-  bool seen[kMaxTiles] = {};
-  int64_t prev = 0;
-  for (int p = 0; p < c->t; ++p) {
-    const int32_t tile = sched->order[p];
-    if (tile < 0 || tile >= c->t || seen[tile]) return fail(c, AGEMM_EINVAL, "schedule order is not a permutation");
-    seen[tile] = true;
-    const int64_t off = sched->offset_ns[p];
-    if (off < 0 || off < prev) return fail(c, AGEMM_EINVAL, "schedule offsets must be non-negative and non-decreasing");
-    const double ticks = (double)off * c->ticks_per_ns;
-    if (ticks > 1.0e9) return fail(c, AGEMM_EINVAL, "schedule offset %lld ns is over 10 s", (long long)off);
-    prev = off;
-    pa.order[p] = tile;
-    pa.offset_ticks[p] = (uint32_t)(ticks + 0.5);
-    if (pa.offset_ticks[p]) pa.has_delay = 1;
-  }
-  return AGEMM_OK;
+  return parse_schedule(sched, c->t, c->ticks_per_ns, pa.order, pa.offset_ticks, &pa.has_delay, &c->last_error);
 }
 
 void base_produce_args(agemm_ctx* c, const void* const* a_shards, ProduceArgs& pa) {
@@ -147,27 +103,11 @@ void base_produce_args(agemm_ctx* c, const void* const* a_shards, ProduceArgs& p
   pa.items_per_tile = c->items_per_tile;
 }
 
-// Orders a new consumer after the previous one (they share the workspace and,
-// for BSP, the gathered buffer) when they are on different streams.
+// Orders a new consumer after the previous consumer call of the context.
 int order_after_consumer(agemm_ctx* c, hipStream_t s) {
-  if (c->consumer_pending && c->consumer_stream != s) {
-    hipError_t e = hipStreamWaitEvent(s, c->last_consumer_ev, 0);
-    if (e != hipSuccess) return hip_fail(c, e, "hipStreamWaitEvent");
-  }
-  return AGEMM_OK;
+  const hipError_t e = c->so.before_consumer(s);
+  return e == hipSuccess ? AGEMM_OK : hip_fail(c, e, "hipStreamWaitEvent");
 }
-
-// Records `ev` after a consumer call on stream s.
-int mark_consumer(agemm_ctx* c, hipStream_t s, hipEvent_t ev) {
-  hipError_t e = hipEventRecord(ev, s);
-  if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
-  c->last_consumer_ev = ev;
-  c->consumer_stream = s;
-  c->consumer_pending = true;
-  return AGEMM_OK;
-}
-
-LaunchTiming next_timing(agemm_ctx* c);
 
 // Launches the GEMM (a4-a6 of the path) with the given A source and gate.
 int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* B, void* C, hipStream_t s) {
@@ -188,7 +128,7 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.split_ws = c->mws;
   g.split_cnt = c->mcnt;
   const bool f32 = c->c_dtype == AGEMM_F32;
-  const LaunchTiming t = next_timing(c);
+  const LaunchTiming t = c->timer.next();
   hipError_t e;
   if (c->ws) {
     SmallMArgs sa{};
@@ -204,17 +144,6 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   return AGEMM_OK;
 }
 
-// The events for the next consumer launch (none when timing is off or full).
-LaunchTiming next_timing(agemm_ctx* c) {
-  LaunchTiming t;
-  if (c->timing_on && c->timing_count < c->timing_cap) {
-    t.start = c->timing_events[2 * c->timing_count];
-    t.stop = c->timing_events[2 * c->timing_count + 1];
-    c->timing_count++;
-  }
-  return t;
-}
-
 Gate no_gate(agemm_ctx* c) {
   Gate g{};
   g.flags = nullptr;
@@ -224,15 +153,8 @@ Gate no_gate(agemm_ctx* c) {
   return g;
 }
 
-void free_timing(agemm_ctx* c) {
-  for (hipEvent_t e : c->timing_events) (void)hipEventDestroy(e);
-  c->timing_events.clear();
-  c->timing_cap = c->timing_count = 0;
-  c->timing_on = false;
-}
-
 void free_all(agemm_ctx* c) {
-  free_timing(c);
+  c->timer.destroy();
   if (c->inbox[0]) (void)hipFree(c->inbox[0]);
   if (c->ctrl) (void)hipFree(c->ctrl);
   if (c->gathered) (void)hipFree(c->gathered);
@@ -241,20 +163,14 @@ void free_all(agemm_ctx* c) {
   if (c->mws) (void)hipFree(c->mws);
   if (c->mcnt) (void)hipFree(c->mcnt);
   if (c->err_host) (void)hipHostFree(c->err_host);
-  if (c->ev_consumer) (void)hipEventDestroy(c->ev_consumer);
-  if (c->ev_producer) (void)hipEventDestroy(c->ev_producer);
-  for (int i = 0; i < 2; ++i)
-    if (c->ev_fused[i]) (void)hipEventDestroy(c->ev_fused[i]);
+  c->so.destroy();
 }
 
 }  // namespace
 
 extern "C" {
 
-const char* agemm_status_string(int status) {
-  if (status < 0 || status > AGEMM_ESTATE) return "AGEMM_UNKNOWN";
-  return kStatusNames[status];
-}
+const char* agemm_status_string(int status) { return status_name(status); }
 
 const char* agemm_last_error(const agemm_ctx* ctx) {
   if (!ctx) return "no context";
@@ -324,6 +240,15 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   }
   c->timeout_ticks = (uint64_t)((double)timeout_us * 1000.0 * c->ticks_per_ns);
   if (const char* env = std::getenv("AGEMM_STRICT_ACQUIRE")) c->strict_acquire = std::atoi(env) != 0;
+  // The push producer runs beside the consumer: a persistent grid of half as
+  // many workgroups as CUs copies the items in release order instead of one
+  // workgroup per item flooding every CU. AGEMM_PRODUCER_WGS overrides (0 =
+  // one workgroup per item).
+  c->producer_wgs = c->num_cus / 2;
+  if (const char* env = std::getenv("AGEMM_PRODUCER_WGS")) {
+    const int v = std::atoi(env);
+    if (v >= 0 && v <= 65536) c->producer_wgs = v;
+  }
   if (const char* env = std::getenv("AGEMM_TILE_CONFIG")) {
     const int v = std::atoi(env);
     if (v >= 0 && v < mfma_config_count()) c->tile_config = v;
@@ -383,9 +308,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     e = hipHostGetDevicePointer(&dp, hp, 0);
     c->err_dev = static_cast<ErrWord*>(dp);
   }
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_consumer, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming);
-  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_fused[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = c->so.create();
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     free_all(c);
@@ -429,6 +352,37 @@ int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split) {
   return AGEMM_OK;
 }
 
+int agemm_consumer_info(const agemm_ctx* ctx, agemm_consumer_desc* out) {
+  if (!ctx || !out) return AGEMM_EINVAL;
+  agemm_consumer_desc d{};
+  if (ctx->ws) {
+    const SmallMPlan& p = ctx->small_plan;
+    const int64_t items = (int64_t)p.ranges * p.nblk;
+    d.kind = 1;
+    d.tile_config = -1;
+    d.tiles = (int32_t)items;
+    d.grid = (int32_t)std::min<int64_t>(items, (int64_t)p.wg_per_cu * ctx->num_cus);
+    d.tiles_per_wg = (int32_t)((items + d.grid - 1) / d.grid);
+    d.ranges = p.ranges;
+  } else {
+    const MfmaPlan& p = ctx->mplan;
+    // arrival order runs whole tiles with the default B policy
+    const bool arrival = ctx->order == AGEMM_ORDER_ARRIVAL;
+    const MfmaPlan q = arrival && p.split ? mfma_plan(ctx->M, ctx->N, ctx->W, ctx->num_cus, ctx->tile_config, 0) : p;
+    d.kind = 0;
+    d.tile_config = q.cfg;
+    d.block_m = (int32_t)q.bm;
+    d.block_n = (int32_t)q.bn;
+    d.tiles = (int32_t)q.tiles;
+    d.grid = (int32_t)q.grid;
+    d.split = q.split ? 1 : 0;
+    d.b_nontemporal = q.bnt && !arrival ? 1 : 0;
+    d.tiles_per_wg = q.split ? 1 : (int32_t)((q.tiles + q.grid - 1) / q.grid);
+  }
+  *out = d;
+  return AGEMM_OK;
+}
+
 int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
                     int32_t* grid, int32_t* split) {
   if (M < 1 || N < 8 || W < 1 || W > kMaxShards || num_cus < 1 || tile_config < -1 ||
@@ -445,6 +399,13 @@ int agemm_set_order(agemm_ctx* ctx, int order) {
   if (!ctx) return AGEMM_EINVAL;
   if (order != AGEMM_ORDER_SHARD && order != AGEMM_ORDER_ARRIVAL) return fail(ctx, AGEMM_EINVAL, "unknown order %d", order);
   ctx->order = order;
+  return AGEMM_OK;
+}
+
+int agemm_set_strict_acquire(agemm_ctx* ctx, int strict) {
+  if (!ctx) return AGEMM_EINVAL;
+  if (strict != 0 && strict != 1) return fail(ctx, AGEMM_EINVAL, "strict must be 0 or 1, got %d", strict);
+  ctx->strict_acquire = strict;
   return AGEMM_OK;
 }
 
@@ -466,10 +427,7 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   // This epoch's inbox may be overwritten only once the fused consumers that
   // last read it (two epochs ago) are done; producers run in order.
   const int slot = (int)((ctx->epoch + 1) & 1u);
-  hipError_t e = hipSuccess;
-  if (ctx->fused_pending[slot] && ctx->fused_stream[slot] != s) e = hipStreamWaitEvent(s, ctx->ev_fused[slot], 0);
-  if (e == hipSuccess && ctx->producer_pending && ctx->producer_stream != s)
-    e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
+  hipError_t e = ctx->so.before_produce(slot, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_produce_args(ctx, a_shards, pa);
   pa.dst = ctx->inbox[slot];
@@ -478,16 +436,13 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   pa.flags = ctx->flags[slot];
   pa.t0 = ctx->t0_fused;
   pa.parity = ctx->parity_fused & 1u;
-  e = launch_produce(pa, s);
+  e = launch_produce(pa, ctx->producer_wgs, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "producer launch");
   if (pa.has_delay) ctx->parity_fused++;
-  e = hipEventRecord(ctx->ev_producer, s);
+  e = ctx->so.after_produce(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
-  ctx->producer_pending = true;
-  ctx->producer_stream = s;
   ctx->epoch++;
   ctx->slot_epochs[slot]++;
-  ctx->consumed_this_epoch = false;
   return AGEMM_OK;
 }
 
@@ -510,11 +465,8 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   gate.strict = ctx->strict_acquire;
   rc = launch_gemm(ctx, src, gate, B, C, s);
   if (rc) return rc;
-  ctx->consumed_this_epoch = true;
-  rc = mark_consumer(ctx, s, ctx->ev_fused[slot]);
-  if (rc) return rc;
-  ctx->fused_pending[slot] = true;
-  ctx->fused_stream[slot] = s;
+  const hipError_t e = ctx->so.after_fused(slot, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   return AGEMM_OK;
 }
 
@@ -538,7 +490,7 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   pa.flags = nullptr;
   pa.t0 = ctx->t0_bsp;
   pa.parity = ctx->parity_bsp & 1u;
-  hipError_t e = launch_produce(pa, s);
+  hipError_t e = launch_produce(pa, 0, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "gather launch");
   if (pa.has_delay) ctx->parity_bsp++;
   // 2) the bulk-synchronous barrier
@@ -552,7 +504,8 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   src.lda = ctx->K;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
-  return mark_consumer(ctx, s, ctx->ev_consumer);
+  const hipError_t eo = ctx->so.after_other(s);
+  return eo == hipSuccess ? AGEMM_OK : hip_fail(ctx, eo, "hipEventRecord");
 }
 
 int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, void* stream) {
@@ -568,41 +521,18 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
   src.lda = ctx->KS;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
-  return mark_consumer(ctx, s, ctx->ev_consumer);
+  const hipError_t eo = ctx->so.after_other(s);
+  return eo == hipSuccess ? AGEMM_OK : hip_fail(ctx, eo, "hipEventRecord");
 }
 
 int agemm_timing_begin(agemm_ctx* ctx, int32_t max_launches) {
   if (!ctx) return AGEMM_EINVAL;
-  if (max_launches < 1 || max_launches > 100000) return fail(ctx, AGEMM_EINVAL, "max_launches must be in 1..100000");
-  if (ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing already active");
-  if ((int32_t)ctx->timing_events.size() < 2 * max_launches) {
-    while ((int32_t)ctx->timing_events.size() < 2 * max_launches) {
-      hipEvent_t e = nullptr;
-      const hipError_t rc = hipEventCreate(&e);
-      if (rc != hipSuccess) return hip_fail(ctx, rc, "hipEventCreate");
-      ctx->timing_events.push_back(e);
-    }
-  }
-  ctx->timing_cap = max_launches;
-  ctx->timing_count = 0;
-  ctx->timing_on = true;
-  return AGEMM_OK;
+  return ctx->timer.begin(max_launches, &ctx->last_error);
 }
 
 int agemm_timing_end(agemm_ctx* ctx, float* us, int32_t max, int32_t* count) {
   if (!ctx) return AGEMM_EINVAL;
-  if (!ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing not active");
-  ctx->timing_on = false;
-  const int32_t n = ctx->timing_count;
-  if (count) *count = n;
-  for (int32_t i = 0; i < n; ++i) {
-    hipError_t e = hipEventSynchronize(ctx->timing_events[2 * i + 1]);
-    float ms = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ctx->timing_events[2 * i], ctx->timing_events[2 * i + 1]);
-    if (e != hipSuccess) return hip_fail(ctx, e, "kernel timing events");
-    if (us && i < max) us[i] = ms * 1000.f;
-  }
-  return AGEMM_OK;
+  return ctx->timer.end(us, max, count, &ctx->last_error);
 }
 
 int agemm_check(agemm_ctx* ctx) {

@@ -64,6 +64,7 @@ struct MfmaPlan {
   int64_t tiles = 0;     // output tiles
   int64_t grid = 0;      // workgroups of the persistent grid
   bool split = false;
+  bool bnt = false;      // B's direct loads nontemporal (one row block, whole tiles, shard order)
   size_t ws_bytes = 0;   // split partial slots
   size_t cnt_bytes = 0;  // split counters
 };
@@ -114,7 +115,9 @@ struct LaunchTiming {
   hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_produce(const ProduceArgs& a, hipStream_t s);
+// max_workgroups > 0: a persistent grid of at most that many workgroups walks
+// the items in release order; 0: one workgroup per item.
+hipError_t launch_produce(const ProduceArgs& a, int max_workgroups, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 int mfma_config_count();
 int mfma_config_for(int64_t M, int tile_config);  // configuration launch_gemm_mfma uses

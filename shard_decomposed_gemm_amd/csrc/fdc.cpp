@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "fd_internal.h"
+#include "host_common.h"
 
 using namespace agemm;
 
@@ -39,24 +40,15 @@ struct fdc_ctx {
   uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox
   uint32_t parity_fused = 0, parity_bsp = 0;
 
-  hipEvent_t ev_producer = nullptr;
-  hipEvent_t ev_fused[2] = {nullptr, nullptr};
-  hipEvent_t ev_bsp = nullptr;
-  hipStream_t producer_stream = nullptr, fused_stream[2] = {nullptr, nullptr}, bsp_stream = nullptr;
-  bool producer_pending = false, fused_pending[2] = {false, false}, bsp_pending = false;
-
-  std::vector<hipEvent_t> timing_events;
-  int32_t timing_cap = 0, timing_count = 0;
-  bool timing_on = false;
+  StreamOrder so;     // ordering between calls on different streams
+  KernelTimer timer;  // fdc_timing_begin/end
 
   std::string last_error;
 };
 
 namespace {
 
-const char* kNames[] = {"AGEMM_OK", "AGEMM_EINVAL", "AGEMM_ESHAPE", "AGEMM_ENOMEM",
-                        "AGEMM_EHIP", "AGEMM_ETIMEOUT", "AGEMM_ESTATE"};
-
+int fail(fdc_ctx* c, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
 int fail(fdc_ctx* c, int code, const char* fmt, ...) {
   if (c) {
     char buf[512];
@@ -64,16 +56,12 @@ int fail(fdc_ctx* c, int code, const char* fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    c->last_error = std::string(kNames[code]) + ": " + buf;
+    set_error(&c->last_error, code, "%s", buf);
   }
   return code;
 }
 
-int hip_fail(fdc_ctx* c, hipError_t e, const char* what) {
-  return fail(c, AGEMM_EHIP, "%s: %s", what, hipGetErrorString(e));
-}
-
-bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int hip_fail(fdc_ctx* c, hipError_t e, const char* what) { return set_hip_error(&c->last_error, e, what); }
 
 int check_parts(fdc_ctx* c, const void* const* o_parts, const void* const* lse_parts) {
   if (!o_parts || !lse_parts) return fail(c, AGEMM_EINVAL, "o_parts and lse_parts must be non-NULL");
@@ -84,30 +72,7 @@ int check_parts(fdc_ctx* c, const void* const* o_parts, const void* const* lse_p
 }
 
 int fill_schedule(fdc_ctx* c, const agemm_schedule* sched, FdProduceArgs& pa) {
-  pa.has_delay = 0;
-  for (int p = 0; p < c->t; ++p) {
-    pa.order[p] = p;
-    pa.offset_ticks[p] = 0;
-  }
-  if (!sched) return AGEMM_OK;
-  if (sched->n != c->t || !sched->order || !sched->offset_ns)
-    return fail(c, AGEMM_EINVAL, "schedule must have n == T (%d) entries and non-NULL arrays", c->t);
-  bool seen[kMaxTiles] = {};
-  int64_t prev = 0;
-  for (int p = 0; p < c->t; ++p) {
-    const int32_t tile = sched->order[p];
-    if (tile < 0 || tile >= c->t || seen[tile]) return fail(c, AGEMM_EINVAL, "schedule order is not a permutation");
-    seen[tile] = true;
-    const int64_t off = sched->offset_ns[p];
-    if (off < 0 || off < prev) return fail(c, AGEMM_EINVAL, "schedule offsets must be non-negative and non-decreasing");
-    const double ticks = (double)off * c->ticks_per_ns;
-    if (ticks > 1.0e9) return fail(c, AGEMM_EINVAL, "schedule offset %lld ns is over 10 s", (long long)off);
-    prev = off;
-    pa.order[p] = tile;
-    pa.offset_ticks[p] = (uint32_t)(ticks + 0.5);
-    if (pa.offset_ticks[p]) pa.has_delay = 1;
-  }
-  return AGEMM_OK;
+  return parse_schedule(sched, c->t, c->ticks_per_ns, pa.order, pa.offset_ticks, &pa.has_delay, &c->last_error);
 }
 
 void base_args(fdc_ctx* c, const void* const* o_parts, const void* const* lse_parts, FdProduceArgs& pa) {
@@ -116,16 +81,6 @@ void base_args(fdc_ctx* c, const void* const* o_parts, const void* const* lse_pa
     pa.o_src[s] = s < c->L.W ? static_cast<const float*>(o_parts[s]) : nullptr;
     pa.lse_src[s] = s < c->L.W ? static_cast<const float*>(lse_parts[s]) : nullptr;
   }
-}
-
-LaunchTiming next_timing(fdc_ctx* c) {
-  LaunchTiming t;
-  if (c->timing_on && c->timing_count < c->timing_cap) {
-    t.start = c->timing_events[2 * c->timing_count];
-    t.stop = c->timing_events[2 * c->timing_count + 1];
-    c->timing_count++;
-  }
-  return t;
 }
 
 int launch_combine(fdc_ctx* c, const char* src, const uint32_t* flags, uint32_t target, void* O, hipStream_t s) {
@@ -137,22 +92,18 @@ int launch_combine(fdc_ctx* c, const char* src, const uint32_t* flags, uint32_t 
   a.target = target;
   a.timeout_ticks = c->timeout_ticks;
   a.err = c->err_dev;
-  const hipError_t e = launch_fd_combine(a, c->out_dtype == AGEMM_F32, s, next_timing(c));
+  const hipError_t e = launch_fd_combine(a, c->out_dtype == AGEMM_F32, s, c->timer.next());
   if (e != hipSuccess) return hip_fail(c, e, "combine launch");
   return AGEMM_OK;
 }
 
 void free_all(fdc_ctx* c) {
-  for (hipEvent_t e : c->timing_events) (void)hipEventDestroy(e);
-  c->timing_events.clear();
+  c->timer.destroy();
   if (c->inbox[0]) (void)hipFree(c->inbox[0]);
   if (c->gathered) (void)hipFree(c->gathered);
   if (c->ctrl) (void)hipFree(c->ctrl);
   if (c->err_host) (void)hipHostFree(c->err_host);
-  if (c->ev_producer) (void)hipEventDestroy(c->ev_producer);
-  if (c->ev_bsp) (void)hipEventDestroy(c->ev_bsp);
-  for (int i = 0; i < 2; ++i)
-    if (c->ev_fused[i]) (void)hipEventDestroy(c->ev_fused[i]);
+  c->so.destroy();
 }
 
 }  // namespace
@@ -215,9 +166,7 @@ int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dty
     e = hipHostGetDevicePointer(&dp, hp, 0);
     c->err_dev = static_cast<ErrWord*>(dp);
   }
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_bsp, hipEventDisableTiming);
-  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_fused[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = c->so.create();
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     free_all(c);
@@ -261,10 +210,7 @@ int fdc_produce(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
   hipStream_t s = static_cast<hipStream_t>(stream);
   // The inbox of this epoch was last read by the fused combine two epochs ago.
   const int slot = (int)((ctx->epoch + 1) & 1u);
-  hipError_t e = hipSuccess;
-  if (ctx->fused_pending[slot] && ctx->fused_stream[slot] != s) e = hipStreamWaitEvent(s, ctx->ev_fused[slot], 0);
-  if (e == hipSuccess && ctx->producer_pending && ctx->producer_stream != s)
-    e = hipStreamWaitEvent(s, ctx->ev_producer, 0);
+  hipError_t e = ctx->so.before_produce(slot, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_args(ctx, o_parts, lse_parts, pa);
   pa.dst = ctx->inbox[slot];
@@ -274,10 +220,8 @@ int fdc_produce(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
   e = launch_fd_produce(pa, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "producer launch");
   if (pa.has_delay) ctx->parity_fused++;
-  e = hipEventRecord(ctx->ev_producer, s);
+  e = ctx->so.after_produce(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
-  ctx->producer_pending = true;
-  ctx->producer_stream = s;
   ctx->epoch++;
   ctx->slot_epochs[slot]++;
   return AGEMM_OK;
@@ -289,13 +233,16 @@ int fdc_run_fused(fdc_ctx* ctx, void* O, void* stream) {
   if (ctx->epoch == 0) return fail(ctx, AGEMM_ESTATE, "run_fused before any produce");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int slot = (int)(ctx->epoch & 1u);
+  // After the previous combine of this context, whatever its stream: the
+  // producer of a later epoch waits only for the last fused combine of an
+  // inbox, so an earlier reader of that inbox must be done by then.
+  hipError_t e = ctx->so.before_consumer(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   // One increment per tile per epoch on this inbox (wraps with the counters).
   int rc = launch_combine(ctx, ctx->inbox[slot], ctx->flags[slot], ctx->slot_epochs[slot], O, s);
   if (rc) return rc;
-  const hipError_t e = hipEventRecord(ctx->ev_fused[slot], s);
+  e = ctx->so.after_fused(slot, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
-  ctx->fused_pending[slot] = true;
-  ctx->fused_stream[slot] = s;
   return AGEMM_OK;
 }
 
@@ -309,9 +256,9 @@ int fdc_run_bsp(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
   rc = fill_schedule(ctx, sched, pa);
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The gather buffer is shared by baseline calls: wait for the last one's combine.
-  hipError_t e = hipSuccess;
-  if (ctx->bsp_pending && ctx->bsp_stream != s) e = hipStreamWaitEvent(s, ctx->ev_bsp, 0);
+  // After the previous combine of this context (the gather buffer is shared by
+  // baseline calls).
+  hipError_t e = ctx->so.before_consumer(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   // 1) all-gather stand-in: every partial into the gather buffer
   base_args(ctx, o_parts, lse_parts, pa);
@@ -330,43 +277,19 @@ int fdc_run_bsp(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
   // 3) the same combine with the flags off
   rc = launch_combine(ctx, ctx->gathered, nullptr, 0, O, s);
   if (rc) return rc;
-  e = hipEventRecord(ctx->ev_bsp, s);
+  e = ctx->so.after_other(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
-  ctx->bsp_pending = true;
-  ctx->bsp_stream = s;
   return AGEMM_OK;
 }
 
 int fdc_timing_begin(fdc_ctx* ctx, int32_t max_launches) {
   if (!ctx) return AGEMM_EINVAL;
-  if (max_launches < 1 || max_launches > 100000) return fail(ctx, AGEMM_EINVAL, "max_launches must be in 1..100000");
-  if (ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing already active");
-  while ((int32_t)ctx->timing_events.size() < 2 * max_launches) {
-    hipEvent_t ev = nullptr;
-    const hipError_t e = hipEventCreate(&ev);
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventCreate");
-    ctx->timing_events.push_back(ev);
-  }
-  ctx->timing_cap = max_launches;
-  ctx->timing_count = 0;
-  ctx->timing_on = true;
-  return AGEMM_OK;
+  return ctx->timer.begin(max_launches, &ctx->last_error);
 }
 
 int fdc_timing_end(fdc_ctx* ctx, float* us, int32_t max, int32_t* count) {
   if (!ctx) return AGEMM_EINVAL;
-  if (!ctx->timing_on) return fail(ctx, AGEMM_ESTATE, "timing not active");
-  ctx->timing_on = false;
-  const int32_t n = ctx->timing_count;
-  if (count) *count = n;
-  for (int32_t i = 0; i < n; ++i) {
-    hipError_t e = hipEventSynchronize(ctx->timing_events[2 * i + 1]);
-    float ms = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ctx->timing_events[2 * i], ctx->timing_events[2 * i + 1]);
-    if (e != hipSuccess) return hip_fail(ctx, e, "kernel timing events");
-    if (us && i < max) us[i] = ms * 1000.f;
-  }
-  return AGEMM_OK;
+  return ctx->timer.end(us, max, count, &ctx->last_error);
 }
 
 int fdc_check(fdc_ctx* ctx) {

@@ -44,6 +44,7 @@
 // rest is issue stalls of the one wave per SIMD (fragment-read and
 // direct-load waits, the per-k-step barrier).
 #include "agemm_internal.h"
+#include "mfma_sched.h"
 
 #include <algorithm>
 
@@ -64,9 +65,8 @@ __device__ inline uint64_t uniform_mask(uint64_t mask) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(mask >> 32));
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
-__device__ inline int swz_b(int k) { return (k & 3) << 2; }
-template <int CPR>
-__device__ inline int swz_a(int row) { return (row / (16 / CPR)) % CPR; }
+using sched::swz_a;
+using sched::swz_b;
 
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   static_assert(!ARRIVAL || (GATED && !SPLIT), "arrival order is a mode of the gated whole-tile consumer");
   using S = Shape<BM, BN, BK, WM, WN>;
   constexpr int NT = S::NT, TM = S::TM, TN = S::TN, FM = S::FM, FN = S::FN, LOADS = S::LOADS;
-  constexpr int CPR_A = S::CPR_A, CPR_B = S::CPR_B, KSUB = S::KSUB, NMF = S::NMF, NR = S::NR, LPS = S::LPS;
+  constexpr int CPR_A = S::CPR_A, KSUB = S::KSUB, NMF = S::NMF, NR = S::NR, LPS = S::LPS;
   constexpr bool AGPR = S::AGPR;
   constexpr int ROWA = BK * 2;
   static_assert(STAGES >= 2 && STAGES * S::STAGE <= 160 * 1024, "LDS budget");
@@ -213,58 +213,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   const int wn = wave - wm * WN;
 
   const int64_t M = g.M, N = g.N;
-  const int MB = (int)((M + BM - 1) / BM);
-  const int NB = (int)((N + BN - 1) / BN);
-  const int total = MB * NB;
   const int SPS = (int)(g.KS / BK);
   const int NS = (int)(g.K / BK);
   const int G = gridDim.x;
-  const bool xcd_split = (total % 8 == 0) && (G % 8 == 0);
-
-  // Work of this workgroup as segments: a tile and its k-steps [kb, ke).
-  // Without the split, tiles blockIdx.x, blockIdx.x + G, ... in full. With
-  // it, the units [u0, u1) of the workgroup's run (unit = (tile, shard),
-  // tile-major; the run of workgroup b is [floor(b*U/G), floor((b+1)*U/G))),
-  // cut at tile borders, so only the first and last segments can be partial.
-  // Runs are numbered so that consecutive runs share an XCD (workgroups are
-  // dealt round-robin to the 8 XCDs) and work on neighbouring tiles.
+  const sched::TileGrid tg = sched::tile_grid(M, N, BM, BN, G);
+  // Work of this workgroup as segments (a tile and its k-steps), whole tiles
+  // or the stream-K split's run of (tile, shard) units: see mfma_sched.h.
   const int Wsh = g.W;
-  const int64_t U = (int64_t)total * Wsh;
-  const int bp = (SPLIT && G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int64_t u0 = (int64_t)bp * U / G, u1 = (int64_t)(bp + 1) * U / G;
-  struct Seg {
-    int w, kb, ke;
-  };
-  auto seg_end = [&](int w) {
-    const int64_t e = u1 < (int64_t)(w + 1) * Wsh ? u1 : (int64_t)(w + 1) * Wsh;
-    return (int)(e - (int64_t)w * Wsh) * SPS;
-  };
-  auto seg_first = [&](Seg& q) {
-    if constexpr (SPLIT) {
-      q.w = (int)(u0 / Wsh);
-      q.kb = (int)(u0 - (int64_t)q.w * Wsh) * SPS;
-      q.ke = seg_end(q.w);
-    } else {
-      q.w = blockIdx.x;
-      q.kb = 0;
-      q.ke = NS;
-    }
-  };
-  // Advances q to the next segment; false (q unchanged) when there is none.
-  auto seg_next = [&](Seg& q) -> bool {
-    if constexpr (SPLIT) {
-      const int w = q.w + 1;
-      if ((int64_t)w * Wsh >= u1) return false;
-      q.w = w;
-      q.kb = 0;
-      q.ke = seg_end(w);
-    } else {
-      const int w = q.w + G;
-      if (w >= total) return false;
-      q.w = w;
-    }
-    return true;
-  };
+  const sched::Work wk = sched::work_of((int)blockIdx.x, G, tg.total, Wsh, SPS, SPLIT);
+  const int bp = wk.bp;
+  using Seg = sched::Seg;
+  auto seg_first = [&](Seg& q) { sched::seg_first(wk, q); };
+  auto seg_next = [&](Seg& q) -> bool { return sched::seg_next(wk, q); };
 
   // LDS read offsets, fixed for the launch. B (transpose read, 16-lane
   // groups): lane supplies row k = 16*ks + 8*(g/2) + 4*h + (i/4) and columns
@@ -295,9 +255,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   // keeps the count of loads in flight, and so every wait, uniform.
   Seg cseg;                                  // segment of the cursor
   seg_first(cseg);
-  int ct = 0, cs = 0, cts = 0;               // k-step in the tile, shard, k-step in the shard
-  int cft = 0, cfsub = 0;                    // flag tile, k-step within it
+  sched::KPos kp{};                          // shard order: position and next event step
+  int ct = 0, cfsub = 0;                     // arrival order: k-step in the tile and in its flag tile
   const int spt = SPS / g.gate.kt;
+  bool track = GATED;                        // a flag of this launch may still be unseen
   const char* cb = nullptr;
   const char* ca = nullptr;
   int64_t a_row0 = 0;
@@ -324,7 +285,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   int wslot = 0, rslot = 0;
   bool pending = false;  // a choice waits to be applied after the next barrier
   int64_t c_n0 = 0;
-  const uint64_t tmask = g.gate.t >= 64 ? ~0ull : ((1ull << g.gate.t) - 1ull);
+  const uint64_t tmask = sched::flag_mask(g.gate.t);
   auto gate = [&](const int tile) {
     if constexpr (GATED) {
       // Fast path (tile already seen, or given up) falls through without a
@@ -366,20 +327,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       ready = uniform_mask(mask);
     }
   };
-  // Tile w -> (m0, n0). Workgroups are dealt round-robin to the 8 XCDs; each
-  // XCD gets a contiguous range of logical tiles, ordered in groups of 8
-  // row-blocks, so the tiles running together on one XCD share A and B rows
-  // in its L2.
-  // (With the split, w is already a logical index: the runs are numbered by XCD.)
   auto tile_coords = [&](int w, int64_t& m0, int64_t& n0) {
-    const int logical = (!SPLIT && xcd_split) ? (w % 8) * (total / 8) + (w / 8) : w;
-    constexpr int GM = 8;
-    const int group = logical / (GM * NB);
-    const int first_m = group * GM;
-    const int gsize = (MB - first_m) < GM ? (MB - first_m) : GM;
-    const int in_group = logical - group * GM * NB;
-    m0 = (int64_t)(first_m + in_group % gsize) * BM;
-    n0 = (int64_t)(in_group / gsize) * BN;
+    int mb, nb;
+    sched::tile_coords(tg, SPLIT, w, mb, nb);
+    m0 = (int64_t)mb * BM;
+    n0 = (int64_t)nb * BN;
   };
   // Arrival order: wave 0's choice of the next flag tile (see above). If no
   // untaken tile comes up within the timeout it takes the lowest untaken one,
@@ -401,8 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
             __builtin_amdgcn_s_sleep(2);
           }
         }
-        if (c == 0) c = ~taken & tmask;
-        if (lane == 0) s_choice[wslot] = (int)__builtin_ctzll(c);
+        if (lane == 0) s_choice[wslot] = sched::arrival_pick(ready, taken, tmask);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
       wslot ^= 1;
@@ -417,22 +368,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     tile_coords(cseg.w, m0, n0);
     const int rmax = (int)(M - 1 - m0);
 #pragma unroll
-    for (int j = 0; j < S::A_ITERS; ++j) {
-      const int q = j * NT + wave * 64 + lane;
-      int r = q / CPR_A;
-      const int c = (q % CPR_A) ^ swz_a<CPR_A>(r);
-      r = r < rmax ? r : rmax;
-      a_off[j] = (uint32_t)(r * lda2 + c * 16);
-    }
+    for (int j = 0; j < S::A_ITERS; ++j) a_off[j] = sched::a_src_offset<BK>(j * NT + wave * 64 + lane, rmax, lda2);
     const int cmax = (int)(N - 8 - n0);
 #pragma unroll
-    for (int j = 0; j < S::B_ITERS; ++j) {
-      const int q = j * NT + wave * 64 + lane;
-      const int k = q / CPR_B;
-      int c = ((q % CPR_B) ^ swz_b(k)) * 8;
-      c = c < cmax ? c : cmax;
-      b_off[j] = (uint32_t)((k * N + c) * 2);
-    }
+    for (int j = 0; j < S::B_ITERS; ++j) b_off[j] = sched::b_src_offset<BN>(j * NT + wave * 64 + lane, cmax, N);
     a_row0 = m0 * lda2;
     if constexpr (ARRIVAL) {
       c_n0 = n0;
@@ -442,15 +381,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       choose();
       return;
     }
-    // A segment starts at a shard border: kb = cs * SPS.
-    ct = cseg.kb;
-    cs = cseg.kb / SPS;
-    cts = 0;
-    cft = cs * g.gate.kt;
-    cfsub = 0;
-    ca = (const char*)g.a.base[cs] + a_row0;
+    // A segment starts at a shard border.
+    sched::kpos_enter(kp, cseg, SPS, spt, g.gate.kt, track);
+    ca = (const char*)g.a.base[kp.cs] + a_row0;
     cb = (const char*)g.B + n0 * 2 + (int64_t)cseg.kb * BK * N * 2;
-    gate(cft);
+    gate(kp.cft);
   };
   // Arrival order: applies the published choice (after a barrier): points the
   // cursor at the flag tile's first k-step and gates it. The choice is one of
@@ -461,19 +396,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     rslot ^= 1;
     pending = false;
     taken |= 1ull << f;
-    cft = f;
-    const int fs = f / g.gate.kt, fk = f - fs * g.gate.kt;
-    ca = (const char*)g.a.base[fs] + a_row0 + (int64_t)fk * spt * BK * 2;
-    cb = (const char*)g.B + c_n0 * 2 + ((int64_t)fs * SPS + (int64_t)fk * spt) * BK * N * 2;
+    const int fs = f / g.gate.kt;
+    const int step = sched::flag_first_step(f, g.gate.kt, SPS, spt);
+    ca = (const char*)g.a.base[fs] + a_row0 + (int64_t)(step - fs * SPS) * BK * 2;
+    cb = (const char*)g.B + c_n0 * 2 + (int64_t)step * BK * N * 2;
     gate(f);
   };
-  auto cursor_advance = [&]() {
-    if (++ct == cseg.ke) {
-      if (seg_next(cseg)) cursor_enter();
-      else ct = cseg.ke - 1;
+  // Shard order: the common k-step is two pointer bumps, a counter and one
+  // branch that is not taken (with one wave per SIMD a taken branch in every
+  // k-step stalls the MFMA issue; the compiler keeps every counter in scalar
+  // registers only with the segment end tested apart from the event step);
+  // shard, flag-tile and segment borders go through cursor_event. Past the
+  // last tile the cursor keeps re-loading the last step into buffers nobody
+  // reads, which keeps the count of loads in flight, and so every wait,
+  // uniform.
+  auto cursor_event = [&]() __attribute__((always_inline)) {
+    if (kp.ct == cseg.ke) {
+      if (seg_next(cseg)) {
+        cursor_enter();
+      } else {
+        ca -= BK * 2;
+        cb -= (int64_t)BK * N * 2;
+        kp.ct = cseg.ke - 1;
+      }
       return;
     }
+    const int ev = sched::kpos_event(kp, cseg.ke, SPS, spt, track);
+    if (ev & sched::kEvShard) ca = (const char*)g.a.base[kp.cs] + a_row0;
+    if (ev & sched::kEvFlag) {
+      gate(kp.cft);
+      // every flag seen raised (or the wait given up): no gate from here on
+      if (__builtin_amdgcn_readfirstlane((int)(((ready & tmask) == tmask) || dead))) track = false;
+    }
+  };
+  auto cursor_advance = [&]() {
     if constexpr (ARRIVAL) {
+      if (++ct == cseg.ke) {
+        if (seg_next(cseg)) cursor_enter();
+        else ct = cseg.ke - 1;
+        return;
+      }
       if (++cfsub == spt) {
         cfsub = 0;
         choose();
@@ -483,19 +445,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       }
       return;
     }
+    ca += BK * 2;
     cb += (int64_t)BK * N * 2;
-    if (++cts == SPS) {
-      cts = 0;
-      ++cs;
-      ca = (const char*)g.a.base[cs] + a_row0;
-    } else {
-      ca += BK * 2;
-    }
-    if (++cfsub == spt) {
-      cfsub = 0;
-      ++cft;
-      gate(cft);
-    }
+    if (__builtin_expect(sched::kpos_step(kp, cseg.ke), 0)) cursor_event();
   };
 
   auto issue_one = [&](int j, int buf) {
@@ -562,11 +514,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   // first and its last tile, in slots 2*b and 2*b + 1; one ticket counter per
   // tile.
   __shared__ uint32_t s_ticket;
-  auto owner = [&](int64_t u) { return (int)(((u + 1) * G - 1) / U); };
-  auto slot_of = [&](int b, int w) {
-    const int first_tile = (int)(((int64_t)b * U / G) / Wsh);
-    return 2 * b + (first_tile == w ? 0 : 1);
-  };
+  auto owner = [&](int64_t u) { return sched::owner(wk, u); };
+  auto slot_of = [&](int b, int w) { return sched::slot_of(wk, b, w); };
   constexpr int SLOT_U64 = BM * BN / 2;  // one slot in 8-byte words
   // Word h of block (fm, fn) of thread tid: contiguous across the workgroup.
   auto slot_word = [&](int fm, int fn, int h) { return ((fm * FN + fn) * 8 + h) * NT + tid; };
@@ -767,12 +716,7 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
   // Arrival order needs a tile to span at least the prologue's steps (the
   // cursor publishes a tile's order at a barrier the prologue does not have).
   const bool arrival = arrival_requested(a) && !p.split && a.K / BK >= STAGES;
-  // One row block: every element of B is read by one tile only, so its loads
-  // skip L2 allocation (M = 128, N = 28672, 224 workgroups: 98.7 against
-  // 101.4 us). With more row blocks, tiles of one XCD share B panels through
-  // the L2; with few workgroups the nontemporal loads streamed slower (32
-  // tiles: 73 against 48 us), so at least half of the CUs must be busy.
-  const bool bnt = BM == 128 && BN == 128 && a.M <= BM && !p.split && !arrival && 2 * p.grid >= a.num_cus;
+  const bool bnt = p.bnt && !arrival;
 #define L4(G_, F_, S_, A_)                                                                                     \
   do {                                                                                                        \
     if (t.start)                                                                                              \
@@ -849,6 +793,13 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, in
   if (split_mode < 0) p.split = W >= 2 && 2 * p.tiles <= num_cus && 2 * run_units <= run_tiles;
   else p.split = split_mode > 0 && W >= 2;
   p.grid = p.split ? g_units : g_tiles;
+  // One row block: every element of B is read by one tile only, so its loads
+  // skip L2 allocation (M = 128, N = 28672, 224 workgroups: 98.7 against
+  // 101.4 us). With more row blocks, tiles of one XCD share B panels through
+  // the L2; with few workgroups the nontemporal loads streamed slower (32
+  // tiles: 73 against 48 us), so at least half of the CUs must be busy.
+  // (Arrival-order launches keep the default policy.)
+  p.bnt = p.cfg == 2 && M <= p.bm && !p.split && 2 * p.grid >= num_cus;
   if (p.split) {
     p.ws_bytes = sizeof(float) * 2 * (size_t)p.grid * (size_t)(p.bm * p.bn);
     p.cnt_bytes = sizeof(uint32_t) * (size_t)p.tiles;

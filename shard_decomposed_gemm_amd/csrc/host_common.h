@@ -1,0 +1,71 @@
+// Host-side pieces shared by the two C-ABI contexts (agemm.cpp for the
+// shard-decomposed GEMM, fdc.cpp for the Flash-Decode combine): status text,
+// argument checks, the producer's release schedule, stream ordering between
+// calls of one context, and kernel timing with events attached to dispatches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "agemm.h"
+#include "agemm_internal.h"
+
+namespace agemm {
+
+// "AGEMM_xxx: message" into *last; returns code.
+int set_error(std::string* last, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+int set_hip_error(std::string* last, hipError_t e, const char* what);
+const char* status_name(int code);
+
+inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a release schedule for T tiles and converts it for the producer:
+// order[p] = tile released p-th, offset_ticks[p] = its release time in
+// wall-clock ticks, *has_delay = any offset non-zero. sched == NULL is tile
+// order with no delay.
+int parse_schedule(const agemm_schedule* sched, int T, double ticks_per_ns, int32_t* order, uint32_t* offset_ticks,
+                   int32_t* has_delay, std::string* last);
+
+// Ordering between the calls of one context on different streams. Two
+// inboxes alternate by epoch; the producer of an epoch waits (device side)
+// for the last fused consumer of its inbox (two epochs ago) and for the
+// previous producer; every consumer call waits for the previous consumer
+// call of the context, of any kind (they share workspaces, and a producer
+// that waits for the last fused consumer of an inbox must thereby wait for
+// every earlier reader of it). One event per call; a wait is skipped when the
+// event was recorded on the waiting stream (in-stream order already holds,
+// and every dependency packet costs command-processor time between kernels).
+struct StreamOrder {
+  hipEvent_t ev_producer = nullptr;
+  hipEvent_t ev_fused[2] = {nullptr, nullptr};  // last fused consumer of each inbox
+  hipEvent_t ev_other = nullptr;                // last non-fused consumer call
+  hipEvent_t last_consumer = nullptr;           // whichever consumer call came last
+  hipStream_t producer_stream = nullptr, fused_stream[2] = {nullptr, nullptr}, consumer_stream = nullptr;
+  bool producer_pending = false, fused_pending[2] = {false, false}, consumer_pending = false;
+
+  hipError_t create();
+  void destroy();
+  hipError_t before_produce(int slot, hipStream_t s);
+  hipError_t after_produce(hipStream_t s);
+  hipError_t before_consumer(hipStream_t s);
+  hipError_t after_fused(int slot, hipStream_t s);
+  hipError_t after_other(hipStream_t s);
+};
+
+// Events attached to the dispatch of each consumer kernel launched while
+// active (its own start and end stamps), up to cap launches.
+struct KernelTimer {
+  std::vector<hipEvent_t> events;  // start, stop pairs
+  int32_t cap = 0, count = 0;
+  bool on = false;
+
+  int begin(int32_t max_launches, std::string* last);
+  LaunchTiming next();
+  int end(float* us, int32_t max, int32_t* out_count, std::string* last);
+  void destroy();
+};
+
+}  // namespace agemm

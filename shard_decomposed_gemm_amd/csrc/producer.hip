@@ -15,10 +15,15 @@
 // [A_0 | ... | A_{W-1}] along K), with plain stores: the kernel boundary
 // publishes them.
 //
-// One workgroup = one work item = rows [q*R, (q+1)*R) of tile (s, kt), with
-// items ordered by release position p. A release schedule makes the item
-// wait until offset_ticks[p] after a start time shared by all workgroups of
-// the launch.
+// Work item = rows [q*R, (q+1)*R) of tile (s, kt), items numbered in release
+// order p. The gather copy runs one workgroup per item (it runs alone and
+// wants the whole GPU). The push runs beside the consumer GEMM: a bounded,
+// persistent grid walks the items in release order (workgroup b takes items
+// b, b + G, ...), so it occupies a few waves per CU instead of flooding every
+// CU with thousands of copy workgroups while the consumer works. A release
+// schedule makes an item wait until offset_ticks[p] after a start time
+// shared by all workgroups of the launch; offsets do not decrease with p, so
+// a workgroup never holds a later item behind an earlier one's delay.
 #include "agemm_internal.h"
 
 namespace agemm {
@@ -29,88 +34,105 @@ constexpr int kProducerThreads = 256;
 
 __device__ inline uint64_t wall_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
+// 16-byte device-coherent stores: a raw buffer store with cache policy sc1
+// (device scope: written through the XCD's L2 to the coherence point), the
+// policy the compiler gives an agent-scope relaxed atomic store, which it only
+// emits up to 8 bytes. The compiler tracks these stores in its wait counts.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kPolicyDeviceScope = 16;  // sc1 = 1, sc0 = 0
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
+
 template <bool FLAGS>
 __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a) {
-  const int item = blockIdx.x;
-  const int p = item / a.items_per_tile;
-  const int q = item - p * a.items_per_tile;
-  const int tile = a.order[p];
-  const int s = tile / a.kt;
-  const int kt = tile - s * a.kt;
+  const int items = a.t * a.items_per_tile;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int p = item / a.items_per_tile;
+    const int q = item - p * a.items_per_tile;
+    const int tile = a.order[p];
+    const int s = tile / a.kt;
+    const int kt = tile - s * a.kt;
 
-  if (a.has_delay) {
-    // Launches with a schedule alternate between two start-time slots; each
-    // clears the other one for the next scheduled launch (stream-ordered).
-    if (threadIdx.x == 0) {
-      const uint64_t now = wall_clock();
-      unsigned long long expected = 0;
-      // The first workgroup to arrive fixes the launch's start time.
-      __hip_atomic_compare_exchange_strong(reinterpret_cast<unsigned long long*>(a.t0 + a.parity), &expected,
-                                           (unsigned long long)now, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t base = expected ? (uint64_t)expected : now;
-      const uint64_t due = base + (uint64_t)a.offset_ticks[p];
-      while (wall_clock() < due) __builtin_amdgcn_s_sleep(8);
-      if (item == 0)
-        __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.t0 + (a.parity ^ 1u)), 0ull, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    if (a.has_delay) {
+      // Launches with a schedule alternate between two start-time slots; each
+      // clears the other one for the next scheduled launch (stream-ordered).
+      if (threadIdx.x == 0) {
+        const uint64_t now = wall_clock();
+        unsigned long long expected = 0;
+        // The first workgroup to arrive fixes the launch's start time.
+        __hip_atomic_compare_exchange_strong(reinterpret_cast<unsigned long long*>(a.t0 + a.parity), &expected,
+                                             (unsigned long long)now, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t base = expected ? (uint64_t)expected : now;
+        const uint64_t due = base + (uint64_t)a.offset_ticks[p];
+        while (wall_clock() < due) __builtin_amdgcn_s_sleep(8);
+        if (item == 0)
+          __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.t0 + (a.parity ^ 1u)), 0ull, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
 
-  const int64_t r0 = (int64_t)q * a.rows_per_item;
-  int64_t r1 = r0 + a.rows_per_item;
-  if (r1 > a.M) r1 = a.M;
-  const int cpr = a.bkf >> 3;  // 16-byte chunks per row segment
-  const int64_t total = (r1 - r0) * cpr;
-  const _Float16* __restrict__ src = a.src[s] + (int64_t)kt * a.bkf;
-  _Float16* __restrict__ dst = a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * a.bkf;
+    const int64_t r0 = (int64_t)q * a.rows_per_item;
+    int64_t r1 = r0 + a.rows_per_item;
+    if (r1 > a.M) r1 = a.M;
+    const int cpr = a.bkf >> 3;  // 16-byte chunks per row segment
+    const int64_t total = (r1 - r0) * cpr;
+    const _Float16* __restrict__ src = a.src[s] + (int64_t)kt * a.bkf;
+    _Float16* __restrict__ dst = a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * a.bkf + r0 * a.dst_ld;
+    // Push: the item's rows of its inbox slot, (r1 - r0 - 1) * KS + bkf elements
+    // (under 64 MiB: an item holds at most 1 MiB of a tile, and KS / bkf <= 64).
+    // (The gather copy stores plainly and leaves the descriptor empty.)
+    const int span = FLAGS ? (int)(((r1 - r0 - 1) * a.dst_ld + a.bkf) * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, span, kRsrcWord3);
 
-  // Four 16-byte chunks in flight per thread (plain registers, no arrays).
-  auto src_at = [&](int64_t cc) {
-    return reinterpret_cast<const uint4*>(src + (r0 + cc / cpr) * a.KS + (cc % cpr) * 8);
-  };
-  auto dst_at = [&](int64_t cc) {
-    return reinterpret_cast<uint4*>(dst + (r0 + cc / cpr) * a.dst_ld + (cc % cpr) * 8);
-  };
-  auto put = [&](int64_t cc, const uint4& v) {
+    // Four 16-byte chunks in flight per thread (plain registers, no arrays).
+    auto src_at = [&](int64_t cc) {
+      return reinterpret_cast<const uint4*>(src + (r0 + cc / cpr) * a.KS + (cc % cpr) * 8);
+    };
+    auto dst_off = [&](int64_t cc) { return (cc / cpr) * a.dst_ld + (cc % cpr) * 8; };  // elements
+    auto put = [&](int64_t cc, const uint4& v) {
+      if constexpr (FLAGS) {
+        const u32x4 x = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, (int)(dst_off(cc) * 2), 0, kPolicyDeviceScope);
+      } else {
+        *reinterpret_cast<uint4*>(dst + dst_off(cc)) = v;
+      }
+    };
+    constexpr int P = kProducerThreads;
+    int64_t c = threadIdx.x;
+    for (; c + 3 * P < total; c += 4 * P) {
+      const uint4 v0 = *src_at(c);
+      const uint4 v1 = *src_at(c + P);
+      const uint4 v2 = *src_at(c + 2 * P);
+      const uint4 v3 = *src_at(c + 3 * P);
+      put(c, v0);
+      put(c + P, v1);
+      put(c + 2 * P, v2);
+      put(c + 3 * P, v3);
+    }
+    for (; c < total; c += P) put(c, *src_at(c));
+
     if constexpr (FLAGS) {
-      uint64_t* d = reinterpret_cast<uint64_t*>(dst_at(cc));
-      __hip_atomic_store(d, ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(d + 1, ((uint64_t)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      *dst_at(cc) = v;
+      // Every thread's device-coherent stores have completed before the
+      // workgroup meets; then one increment publishes the item's part of the
+      // tile. The barrier also keeps the next item's delay wait (thread 0)
+      // behind this item's stores.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.flags + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (a.has_delay) {
+      __syncthreads();  // thread 0's next delay wait starts after this item
     }
-  };
-  constexpr int P = kProducerThreads;
-  int64_t c = threadIdx.x;
-  for (; c + 3 * P < total; c += 4 * P) {
-    const uint4 v0 = *src_at(c);
-    const uint4 v1 = *src_at(c + P);
-    const uint4 v2 = *src_at(c + 2 * P);
-    const uint4 v3 = *src_at(c + 3 * P);
-    put(c, v0);
-    put(c + P, v1);
-    put(c + 2 * P, v2);
-    put(c + 3 * P, v3);
-  }
-  for (; c < total; c += P) put(c, *src_at(c));
-
-  if constexpr (FLAGS) {
-    // Every thread's device-coherent stores have completed before the
-    // workgroup meets; then one increment publishes the tile.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.flags + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 }  // namespace
 
-hipError_t launch_produce(const ProduceArgs& a, hipStream_t s) {
+hipError_t launch_produce(const ProduceArgs& a, int max_workgroups, hipStream_t s) {
   const unsigned items = (unsigned)a.t * (unsigned)a.items_per_tile;
-  if (a.flags) hipLaunchKernelGGL(produce_kernel<true>, dim3(items), dim3(kProducerThreads), 0, s, a);
-  else hipLaunchKernelGGL(produce_kernel<false>, dim3(items), dim3(kProducerThreads), 0, s, a);
+  const unsigned grid = max_workgroups > 0 && (unsigned)max_workgroups < items ? (unsigned)max_workgroups : items;
+  if (a.flags) hipLaunchKernelGGL(produce_kernel<true>, dim3(grid), dim3(kProducerThreads), 0, s, a);
+  else hipLaunchKernelGGL(produce_kernel<false>, dim3(grid), dim3(kProducerThreads), 0, s, a);
   return hipGetLastError();
 }
 
