@@ -196,6 +196,24 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
  * shard buffers; no inbox, no flags, one kernel. */
 int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, void* C, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the Pull
+ * GEMM of agemm_run_pull with no context. C = sum_s A_s . B[s*KS:(s+1)*KS, :]
+ * with the same shapes, layouts, pointer rules and kernels as a context of
+ * this shape (the MFMA kernel on whole tiles only, never the stream-K split).
+ * It allocates nothing: the small-M kernel's split-K workspace is a
+ * file-scope device array of the library (8 MiB of fp32 partials, i.e.
+ * ranges x M x N <= 2,097,152 with up to 8 K-ranges at M <= 8, and 64 KiB of
+ * column counters), held on each device until the process ends. Every call
+ * on one GPU shares that array: calls that overlap on one GPU (concurrent
+ * streams) race and give undefined C; calls in one stream order are fine.
+ * Returns AGEMM_ESHAPE for a shape outside the accepted set or whose
+ * workspace exceeds the array, AGEMM_EINVAL for a bad dtype or pointer,
+ * AGEMM_EHIP for a runtime failure (also on the first call on a device, which
+ * looks up the array's device address). Asynchronous on `stream`. */
+int agemm_pull_noalloc(int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype, const void* const* a_shards,
+                       const void* B, void* C, void* stream);
+
 /* Flag-tile order of later agemm_run_fused calls (default AGEMM_ORDER_SHARD).
  * The AG+GEMM core identity is a plain sum over shards, so the shards' k-tiles
  * may be added in any order. With AGEMM_ORDER_ARRIVAL each output tile takes

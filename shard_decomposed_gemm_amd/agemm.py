@@ -21,7 +21,7 @@ F16, F32 = 0, 1
 EXPORTED = (
     "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_mfma_plan", "agemm_produce", "agemm_run_fused",
     "agemm_run_bsp", "agemm_run_pull", "agemm_set_order", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
-    "agemm_consumer_info", "agemm_set_strict_acquire",
+    "agemm_consumer_info", "agemm_set_strict_acquire", "agemm_pull_noalloc",
     "agemm_check", "agemm_device_info", "agemm_probe_mfma", "agemm_probe_read",
     "agemm_last_error", "agemm_status_string",
 )
@@ -69,6 +69,7 @@ def load() -> ctypes.CDLL:
     lib.agemm_set_order.argtypes = [vp, ctypes.c_int]
     lib.agemm_consumer_info.argtypes = [vp, ctypes.POINTER(ConsumerDesc)]
     lib.agemm_set_strict_acquire.argtypes = [vp, ctypes.c_int]
+    lib.agemm_pull_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
     lib.agemm_set_spin_timeout_us.argtypes = [vp, i64]
     lib.agemm_timing_begin.argtypes = [vp, i32]
     lib.agemm_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
@@ -95,6 +96,21 @@ def mfma_plan(M: int, N: int, W: int, num_cus: int, tile_config: int = -1, split
     if rc != OK:
         raise AgemmError(rc, f"agemm_mfma_plan: {status_string(rc)}")
     return cfg.value, grid.value, bool(split.value)
+
+
+def pull_noalloc(a_shards, B, C, stream=None) -> int:
+    """agemm_pull_noalloc: Pull GEMM with no context and no device allocation. Returns
+    the status code (the caller decides; there is no context to hold an error text)."""
+    import torch
+    W = len(a_shards)
+    M, KS = a_shards[0].shape
+    K, N = B.shape
+    code = {torch.float16: F16, torch.float32: F32}.get(C.dtype)
+    if code is None:
+        raise TypeError("C must be float16 or float32")
+    arr = (ctypes.c_void_p * W)(*[_ptr(a, f"a_shards[{i}]", torch.float16, (M, KS)) for i, a in enumerate(a_shards)])
+    return load().agemm_pull_noalloc(W, M, K, N, code, arr, _ptr(B, "B", torch.float16, (K, N)),
+                                     _ptr(C, "C", None, (M, N)), _stream_handle(stream))
 
 
 def status_string(code: int) -> str:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libagemm.so")
-SOURCES = ["agemm.cpp", "fdc.cpp", "host_common.cpp", "producer.hip", "gemm_mfma.hip", "gemm_small_m.hip", "fd_combine.hip", "probes.hip"]
+SOURCES = ["agemm.cpp", "fdc.cpp", "host_common.cpp", "producer.hip", "gemm_mfma.hip", "gemm_small_m.hip", "fd_combine.hip", "probes.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

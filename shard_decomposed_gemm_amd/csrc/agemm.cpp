@@ -188,13 +188,8 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   if (K > (int64_t{1} << 22) || N > (int64_t{1} << 24)) return AGEMM_ESHAPE;  // 32-bit lane offsets
   int64_t bkf = flag_ktile;
   if (bkf == 0) {
-    bkf = std::min<int64_t>(256, KS);
-    while ((KS / bkf) * W > kMaxTiles) {
-      int64_t next = bkf + 64;
-      while (next <= KS && KS % next) next += 64;
-      if (next > KS) return AGEMM_ESHAPE;
-      bkf = next;
-    }
+    bkf = default_flag_ktile(KS, W);
+    if (bkf == 0) return AGEMM_ESHAPE;
   }
   if (bkf < 64 || bkf % 64 || KS % bkf) return AGEMM_ESHAPE;
   if ((KS / bkf) * W > kMaxTiles) return AGEMM_ESHAPE;

@@ -56,6 +56,20 @@ struct GemmArgs {
   int32_t arrival;
 };
 
+// Default flag k-tile BKf for shard width KS and W shards: min(256, KS),
+// widened to the next multiple of 64 dividing KS until T = W * KS / BKf <= 64;
+// 0 if there is none. (The kernels also use it as a tiling of K when ungated.)
+inline int64_t default_flag_ktile(int64_t KS, int W) {
+  int64_t bkf = KS < 256 ? KS : 256;
+  while ((KS / bkf) * W > kMaxTiles) {
+    int64_t next = bkf + 64;
+    while (next <= KS && KS % next) next += 64;
+    if (next > KS) return 0;
+    bkf = next;
+  }
+  return bkf;
+}
+
 // Launch plan of the MFMA consumer for a shape, fixed when a context is
 // created: tile configuration, grid, and whether the stream-K split is used.
 struct MfmaPlan {
