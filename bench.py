@@ -204,7 +204,7 @@ def run_fd(args):
     Os = [torch.empty((H, D), dtype=torch.float16 if odt == "f16" else torch.float32, device=dev) for _ in range(2)]
     ctx = FdCombine(W, H, D, heads_per_tile=HT, out_dtype=odt)
     sched = synth.schedule(0x7A01, ctx.t, max_delay)
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     torch.cuda.synchronize()
 
     def step(i):
@@ -294,7 +294,6 @@ def run_sweep(args):
     to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).to(dev)
     B0 = to_dev(synth.matrix_f16(0xB002, K, N))
     Bs = [B0, B0.clone()]
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
     rows = []
 
     def timeit(fn, n):
@@ -312,6 +311,7 @@ def run_sweep(args):
         shards = [to_dev(x) for x in synth.shards(synth.matrix_f16(0xA100 + M, M, K), W)]
         Cs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(2)]
         ctx = Context(W, M, K, N, c_dtype="f16")
+        sp, sc = ctx.streams()
 
         def fused_step(i):
             ctx.produce(shards, stream=sp)
@@ -329,6 +329,9 @@ def run_sweep(args):
                 lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], host_sync=False, stream=sc), n))
             r.setdefault("pull_us", []).append(timeit(
                 lambda i: ctx.run_pull(shards, Bs[i & 1], Cs[i & 1], stream=sc), n))
+            ctx.set_strict_acquire(True)
+            r.setdefault("fused_strict_acquire_us", []).append(timeit(fused_step, n))
+            ctx.set_strict_acquire(False)
         ctx.produce(shards)
         torch.cuda.synchronize()
         r["consumer_only_us"] = [timeit(lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), n)]
@@ -341,14 +344,15 @@ def run_sweep(args):
         rows.append(r)
         ctx.close()
         del shards, Cs
-    print("\n| M | consumer | fused | BSP host sync | BSP device dep | Pull | consumer alone | fused vs BSP "
-          "(host / device) |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("\n| M | consumer | fused | fused, strict acquire | BSP host sync | BSP device dep | Pull | consumer alone "
+          "| fused vs BSP (host / device) |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         c = r["consumer"]
         kern = ("small-M" if c["kind"] == "small_m" else
                 f"cfg {c['tile_config']}, {c['tiles']} tiles / {c['grid']} WG" + (", split" if c["split"] else ""))
-        print(f"| {r['M']} | {kern} | {r['fused_us']:.1f} | {r['bsp_host_sync_us']:.1f} | "
+        print(f"| {r['M']} | {kern} | {r['fused_us']:.1f} | {r['fused_strict_acquire_us']:.1f} | "
+              f"{r['bsp_host_sync_us']:.1f} | "
               f"{r['bsp_device_dep_us']:.1f} | {r['pull_us']:.1f} | {r['consumer_only_us']:.1f} | "
               f"{r['bsp_host_sync_us'] / r['fused_us']:.3f}x / {r['bsp_device_dep_us'] / r['fused_us']:.3f}x |")
 
@@ -429,7 +433,7 @@ def main():
     ctx = Context(W, M, K, N, c_dtype=c_dtype)
     ctx.set_order(args.order)
     sched = synth.schedule(0x5005, ctx.t, 20_000) if sched_kind == "random" else None
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()  # a producer / consumer pair verified to run concurrently
     if args.one_stream:
         sp = sc
     torch.cuda.synchronize()

@@ -181,8 +181,8 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
  * on another stream. B: K x N fp16; C: M x N in the context's dtype.
  * HIP maps streams onto a few hardware queues (4 by default); two streams
  * on one queue run their work in submission order, so the consumer then
- * starts only after the whole producer (still correct, no overlap). Streams
- * created one after the other land on different queues. */
+ * starts only after the whole producer (still correct, no overlap):
+ * agemm_streams gives a pair verified to run concurrently. */
 int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream);
 
 /* Bulk-synchronous baseline on the same GPU: a gather kernel copies the
@@ -225,6 +225,18 @@ int agemm_pull_noalloc(int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dty
  * and on the MFMA consumer only; the small-M consumer keeps every K-range
  * resident at once and needs no reordering. EINVAL for an unknown order. */
 int agemm_set_order(agemm_ctx* ctx, int order);
+
+/* A producer stream and a consumer stream, owned by the context (destroyed by
+ * agemm_destroy), on which kernels run concurrently. HIP maps streams onto a
+ * few hardware queues (4 by default); on two streams that share a queue the
+ * fused consumer starts only after the whole producer (correct, but without
+ * the overlap the Push model is for). The first call creates pairs of
+ * non-blocking, default-priority streams and keeps the first pair on which a
+ * probe kernel launched second started while the first (sleeping 100 us)
+ * still ran; later calls return the same pair. Synchronises the device on
+ * the first call (set-up, not hot path). EHIP if no pair overlapped in 8
+ * attempts. */
+int agemm_streams(agemm_ctx* ctx, void** producer, void** consumer);
 
 /* Flag-wait mode of later run_fused calls: 0 = the consumer reads a tile's
  * data after seeing its flag with no fence (no line of the tile was read in

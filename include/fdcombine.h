@@ -88,6 +88,12 @@ int fdc_run_bsp(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
 /* Spin timeout of the flag waits in microseconds (default 2,000,000). */
 int fdc_set_spin_timeout_us(fdc_ctx* ctx, int64_t us);
 
+/* A producer and a consumer stream, owned by the context, on which kernels
+ * run concurrently (as agemm_streams: verified with a probe kernel pair on
+ * the first call, which synchronises the device; EHIP if no pair of new
+ * streams overlapped in 8 attempts). */
+int fdc_streams(fdc_ctx* ctx, void** producer, void** consumer);
+
 /* Kernel timing, as agemm_timing_begin/end: HIP events attached to the
  * dispatch of each combine kernel launched while active (up to
  * max_launches); end synchronises and returns the durations in microseconds. */

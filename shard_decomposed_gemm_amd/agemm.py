@@ -21,7 +21,7 @@ F16, F32 = 0, 1
 EXPORTED = (
     "agemm_create", "agemm_destroy", "agemm_tiles", "agemm_consumer_kernel", "agemm_consumer_grid", "agemm_mfma_plan", "agemm_produce", "agemm_run_fused",
     "agemm_run_bsp", "agemm_run_pull", "agemm_set_order", "agemm_set_spin_timeout_us", "agemm_timing_begin", "agemm_timing_end",
-    "agemm_consumer_info", "agemm_set_strict_acquire", "agemm_pull_noalloc",
+    "agemm_consumer_info", "agemm_set_strict_acquire", "agemm_pull_noalloc", "agemm_streams",
     "agemm_check", "agemm_device_info", "agemm_probe_mfma", "agemm_probe_read",
     "agemm_last_error", "agemm_status_string",
 )
@@ -69,6 +69,7 @@ def load() -> ctypes.CDLL:
     lib.agemm_set_order.argtypes = [vp, ctypes.c_int]
     lib.agemm_consumer_info.argtypes = [vp, ctypes.POINTER(ConsumerDesc)]
     lib.agemm_set_strict_acquire.argtypes = [vp, ctypes.c_int]
+    lib.agemm_streams.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.agemm_pull_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
     lib.agemm_set_spin_timeout_us.argtypes = [vp, i64]
     lib.agemm_timing_begin.argtypes = [vp, i32]
@@ -271,6 +272,16 @@ class Context:
         out["kind"] = "small_m" if d.kind == 1 else "mfma"
         return out
 
+    def streams(self):
+        """agemm_streams: (producer, consumer) torch streams verified to run concurrently,
+        owned by the context (valid until close())."""
+        import torch
+        if getattr(self, "_pair", None) is None:
+            p, c = ctypes.c_void_p(), ctypes.c_void_p()
+            self._raise(self._lib.agemm_streams(self._h, ctypes.byref(p), ctypes.byref(c)), "agemm_streams")
+            self._pair = (torch.cuda.ExternalStream(p.value), torch.cuda.ExternalStream(c.value))
+        return self._pair
+
     def set_strict_acquire(self, strict: bool):
         """Flag-wait mode of later run_fused calls: False = no fence, True = agent-scope acquire."""
         self._raise(self._lib.agemm_set_strict_acquire(self._h, 1 if strict else 0), "agemm_set_strict_acquire")
@@ -296,6 +307,10 @@ class Context:
 
     def close(self):
         if getattr(self, "_h", None):
+            if getattr(self, "_pair", None) is not None:
+                import torch
+                torch.cuda.synchronize()
+                self._pair = None
             self._lib.agemm_destroy(self._h)
             self._h = None
 

@@ -57,6 +57,8 @@ struct agemm_ctx {
   uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox so far
   uint32_t parity_fused = 0, parity_bsp = 0;
 
+  hipStream_t pair[2] = {nullptr, nullptr};  // agemm_streams: producer, consumer (owned)
+  uint64_t* probe_times = nullptr;           // 3 words in ctrl for the overlap probe
   StreamOrder so;      // ordering between calls on different streams
   KernelTimer timer;   // agemm_timing_begin/end
 
@@ -164,6 +166,8 @@ void free_all(agemm_ctx* c) {
   if (c->mcnt) (void)hipFree(c->mcnt);
   if (c->err_host) (void)hipHostFree(c->err_host);
   c->so.destroy();
+  for (int i = 0; i < 2; ++i)
+    if (c->pair[i]) (void)hipStreamDestroy(c->pair[i]);
 }
 
 }  // namespace
@@ -253,7 +257,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   // on the hot path allocates or relies on an unordered memset.
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
-  const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 4 * sizeof(uint64_t);
+  const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 8 * sizeof(uint64_t);  // + probe times
   c->small_plan = small_m_plan(W, M, KS, N, c->num_cus);
   if (const char* env = std::getenv("AGEMM_SMALL_M_PLAN")) {  // "lanes,ranges,wg_per_cu" override
     int l = 0, r = 0, wpc = 0;
@@ -293,6 +297,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   c->flags[1] = c->ctrl + kMaxTiles;
   c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + 2 * kMaxTiles);
   c->t0_bsp = c->t0_fused + 2;
+  c->probe_times = c->t0_bsp + 2;
   void* hp = nullptr;
   e = hipMemset(c->ctrl, 0, ctrl_bytes);
   if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);
@@ -394,6 +399,17 @@ int agemm_set_order(agemm_ctx* ctx, int order) {
   if (!ctx) return AGEMM_EINVAL;
   if (order != AGEMM_ORDER_SHARD && order != AGEMM_ORDER_ARRIVAL) return fail(ctx, AGEMM_EINVAL, "unknown order %d", order);
   ctx->order = order;
+  return AGEMM_OK;
+}
+
+int agemm_streams(agemm_ctx* ctx, void** producer, void** consumer) {
+  if (!ctx || !producer || !consumer) return AGEMM_EINVAL;
+  if (!ctx->pair[0]) {
+    const int rc = find_stream_pair(ctx->pair, ctx->probe_times, ctx->ticks_per_ns, &ctx->last_error);
+    if (rc) return rc;
+  }
+  *producer = ctx->pair[0];
+  *consumer = ctx->pair[1];
   return AGEMM_OK;
 }
 

@@ -138,6 +138,9 @@ int mfma_config_for(int64_t M, int tile_config);  // configuration launch_gemm_m
 // split_mode: -1 = split when it shortens the busiest workgroup's run, 0 = never, 1 = whenever W >= 2.
 MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode);
 hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
+// Overlap probe (probes.hip): times[0..1] = start, end of a kernel that sleeps
+// `ticks` on `first`; times[2] = start of a kernel launched after it on `second`.
+hipError_t launch_overlap_probe(hipStream_t first, hipStream_t second, uint64_t* times, uint64_t ticks);
 int small_m_limit();
 SmallMPlan small_m_plan(int W, int64_t M, int64_t KS, int64_t N, int num_cus);
 // The plan for given lanes / ranges / workgroups per CU, if the kernel takes it.

@@ -40,6 +40,8 @@ struct fdc_ctx {
   uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox
   uint32_t parity_fused = 0, parity_bsp = 0;
 
+  hipStream_t pair[2] = {nullptr, nullptr};  // fdc_streams: producer, consumer (owned)
+  uint64_t* probe_times = nullptr;           // 3 words in ctrl for the overlap probe
   StreamOrder so;     // ordering between calls on different streams
   KernelTimer timer;  // fdc_timing_begin/end
 
@@ -104,6 +106,8 @@ void free_all(fdc_ctx* c) {
   if (c->ctrl) (void)hipFree(c->ctrl);
   if (c->err_host) (void)hipHostFree(c->err_host);
   c->so.destroy();
+  for (int i = 0; i < 2; ++i)
+    if (c->pair[i]) (void)hipStreamDestroy(c->pair[i]);
 }
 
 }  // namespace
@@ -142,7 +146,7 @@ int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dty
   c->timeout_ticks = (uint64_t)(2.0e9 * c->ticks_per_ns);  // 2 s
 
   const size_t inbox_bytes = (size_t)c->t * (size_t)c->L.blk;
-  const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 4 * sizeof(uint64_t);
+  const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 8 * sizeof(uint64_t);  // + probe times
   bool ok = hipMalloc(&c->inbox[0], 2 * inbox_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->gathered, inbox_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->ctrl, ctrl_bytes) == hipSuccess;
@@ -156,6 +160,7 @@ int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dty
   c->flags[1] = c->ctrl + kMaxTiles;
   c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + 2 * kMaxTiles);
   c->t0_bsp = c->t0_fused + 2;
+  c->probe_times = c->t0_bsp + 2;
   void* hp = nullptr;
   e = hipMemset(c->ctrl, 0, ctrl_bytes);
   if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);
@@ -189,6 +194,17 @@ int fdc_destroy(fdc_ctx* ctx) {
 int fdc_tiles(const fdc_ctx* ctx, int32_t* t) {
   if (!ctx) return AGEMM_EINVAL;
   if (t) *t = ctx->t;
+  return AGEMM_OK;
+}
+
+int fdc_streams(fdc_ctx* ctx, void** producer, void** consumer) {
+  if (!ctx || !producer || !consumer) return AGEMM_EINVAL;
+  if (!ctx->pair[0]) {
+    const int rc = find_stream_pair(ctx->pair, ctx->probe_times, ctx->ticks_per_ns, &ctx->last_error);
+    if (rc) return rc;
+  }
+  *producer = ctx->pair[0];
+  *consumer = ctx->pair[1];
   return AGEMM_OK;
 }
 

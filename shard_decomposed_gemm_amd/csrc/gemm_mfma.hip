@@ -534,7 +534,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   #pragma unroll
           for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-      for (int t = ms.kb; t < ms.ke; ++t) {
+      // One k-step; the loop below runs two per iteration (one taken branch
+      // per two k-steps: measured 0.65 % faster at M = 4096 than one per step).
+      auto kstep = [&]() __attribute__((always_inline)) {
         const uint32_t cur = lds0 + buf * S::STAGE;
         const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
         // Substeps 0 .. KSUB-2: MFMAs of this substep, with the next substep's
@@ -579,6 +581,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
           __builtin_amdgcn_sched_barrier(0);
         }
         buf = nbuf;
+      };
+      int t = ms.kb;
+      for (; t + 1 < ms.ke; t += 2) {
+        kstep();
+        kstep();
+      }
+      if constexpr (BK != 32) {  // BK = 32: a segment (whole shards of 64k columns) has an even step count
+        if (t < ms.ke) kstep();
       }
 
       if constexpr (AGPR) {

@@ -61,6 +61,33 @@ int parse_schedule(const agemm_schedule* sched, int T, double ticks_per_ns, int3
   return AGEMM_OK;
 }
 
+int find_stream_pair(hipStream_t pair[2], uint64_t* probe_times, double ticks_per_ns, std::string* last) {
+  std::vector<hipStream_t> spare;
+  const uint64_t ticks = (uint64_t)(100000.0 * ticks_per_ns);
+  hipError_t e = hipSuccess;
+  for (int attempt = 0; attempt < 8 && e == hipSuccess && !pair[0]; ++attempt) {
+    hipStream_t p = nullptr, q = nullptr;
+    e = hipStreamCreateWithFlags(&p, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&q, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipMemset(probe_times, 0, 3 * sizeof(uint64_t));
+    if (e == hipSuccess) e = launch_overlap_probe(p, q, probe_times, ticks);
+    uint64_t t[3] = {0, 0, 0};
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(t, probe_times, sizeof t, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && t[2] != 0 && t[2] < t[1]) {
+      pair[0] = p;
+      pair[1] = q;
+    } else {
+      if (p) spare.push_back(p);
+      if (q) spare.push_back(q);
+    }
+  }
+  for (hipStream_t x : spare) (void)hipStreamDestroy(x);
+  if (e != hipSuccess) return set_hip_error(last, e, "stream pair probe");
+  if (!pair[0]) return set_error(last, AGEMM_EHIP, "no pair of streams ran concurrently in 8 attempts");
+  return AGEMM_OK;
+}
+
 hipError_t StreamOrder::create() {
   hipError_t e = hipEventCreateWithFlags(&ev_producer, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_other, hipEventDisableTiming);

@@ -55,6 +55,13 @@ struct StreamOrder {
   hipError_t after_other(hipStream_t s);
 };
 
+// A producer and a consumer stream on which kernels run concurrently: pairs
+// of new non-blocking, default-priority streams are probed (a kernel that
+// sleeps 100 us on the first, then one on the second that records its start)
+// and the first pair whose second kernel started while the first still ran is
+// kept in pair[0..1]. probe_times: 3 device words. Synchronises the device.
+int find_stream_pair(hipStream_t pair[2], uint64_t* probe_times, double ticks_per_ns, std::string* last);
+
 // Events attached to the dispatch of each consumer kernel launched while
 // active (its own start and end stamps), up to cap launches.
 struct KernelTimer {

@@ -101,7 +101,32 @@ int time_launches(Launch launch, int warmup, int launches, hipStream_t s, double
   return rc;
 }
 
+// Overlap probe of two streams: the first kernel sleeps for `ticks` of the
+// 100 MHz wall clock and records its start and end; the second records its
+// start. Launched on two streams in that order, the second starts before the
+// first ends only if the streams run on different hardware queues.
+__global__ void overlap_probe_first(uint64_t* t, uint64_t ticks) {
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+    t[0] = t0;
+    t[1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+__global__ void overlap_probe_second(uint64_t* t) {
+  if (threadIdx.x == 0) t[2] = __builtin_amdgcn_s_memrealtime();
+}
+
 }  // namespace
+
+hipError_t launch_overlap_probe(hipStream_t first, hipStream_t second, uint64_t* times, uint64_t ticks) {
+  hipLaunchKernelGGL(overlap_probe_first, dim3(1), dim3(64), 0, first, times, ticks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(overlap_probe_second, dim3(1), dim3(64), 0, second, times);
+  return hipGetLastError();
+}
+
 }  // namespace agemm
 
 using namespace agemm;

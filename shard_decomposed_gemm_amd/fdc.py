@@ -13,6 +13,7 @@ from .agemm import F16, F32, OK, AgemmError, _ptr, _stream_handle, make_schedule
 EXPORTED = (
     "fdc_create", "fdc_destroy", "fdc_tiles", "fdc_produce", "fdc_run_fused", "fdc_run_bsp",
     "fdc_set_spin_timeout_us", "fdc_timing_begin", "fdc_timing_end", "fdc_check", "fdc_last_error",
+    "fdc_streams",
 )
 
 _ready = False
@@ -35,6 +36,7 @@ def load() -> ctypes.CDLL:
         lib.fdc_timing_begin.argtypes = [vp, i32]
         lib.fdc_timing_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
         lib.fdc_check.argtypes = [vp]
+        lib.fdc_streams.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         lib.fdc_last_error.argtypes = [vp]
         lib.fdc_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -108,6 +110,16 @@ class FdCombine:
                                           _stream_handle(stream)), "fdc_run_bsp")
         del keep
 
+    def streams(self):
+        """fdc_streams: (producer, consumer) torch streams verified to run concurrently,
+        owned by the context (valid until close())."""
+        import torch
+        if getattr(self, "_pair", None) is None:
+            p, c = ctypes.c_void_p(), ctypes.c_void_p()
+            self._raise(self._lib.fdc_streams(self._h, ctypes.byref(p), ctypes.byref(c)), "fdc_streams")
+            self._pair = (torch.cuda.ExternalStream(p.value), torch.cuda.ExternalStream(c.value))
+        return self._pair
+
     def set_spin_timeout_us(self, us: int):
         self._raise(self._lib.fdc_set_spin_timeout_us(self._h, int(us)), "fdc_set_spin_timeout_us")
 
@@ -126,6 +138,10 @@ class FdCombine:
 
     def close(self):
         if getattr(self, "_h", None):
+            if getattr(self, "_pair", None) is not None:
+                import torch
+                torch.cuda.synchronize()
+                self._pair = None
             self._lib.fdc_destroy(self._h)
             self._h = None
 

@@ -46,7 +46,7 @@ def _poison(ctx, W, M, K):
 
 def _fused_concurrent(ctx, dsh, B, C, schedule):
     import torch
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     ctx.produce(dsh, schedule=schedule, stream=sp)
     ctx.run_fused(B, C, stream=sc)
     torch.cuda.synchronize()
@@ -120,7 +120,7 @@ def test_arrival_epochs_switch_order():
     probs = [gu.random_problem(W, M, K, N, seed=s) for s in (111, 112, 113)]
     refs = [oracle.sharded_gemm(p[1], p[2]) for p in probs]
     ctx = _ctx(W, M, K, N)
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     outs = []
     for e in range(6):
         p = probs[e % 3]

@@ -36,7 +36,7 @@ def _ctx(W, H, D, HT, dtype):
 
 def _fused(ctx, o, lse, O, schedule=None):
     import torch
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     ctx.produce(o, lse, schedule=schedule, stream=sp)
     ctx.run_fused(O, stream=sc)
     torch.cuda.synchronize()
@@ -150,7 +150,7 @@ def test_fd_alternating_epochs():
     refs = [fdo.combine(o, l) for o, l in sets]
     devs = [_dev_parts(o, l) for o, l in sets]
     ctx = _ctx(W, H, D, HT, "f32")
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     outs = []
     for e in range(6):
         k = e % 3
@@ -180,23 +180,12 @@ def test_fd_timeout_reports_and_recovers():
     order = np.arange(ctx.t, dtype=np.int32)
     offs = np.zeros(ctx.t, dtype=np.int64)
     offs[-1] = 30_000_000  # last tile 30 ms late
-    sp = torch.cuda.Stream()
-    for _ in range(4):
-        # a consumer stream on the producer's hardware queue runs after every tile
-        # is out (a correct run with nothing to time out on): try a fresh stream
-        sc = torch.cuda.Stream()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        O = _out(H, D, "f32")
-        ctx.produce(do, dl, schedule=(order, offs), stream=sp)
-        t0.record(sc)
-        ctx.run_fused(O, stream=sc)
-        t1.record(sc)
-        torch.cuda.synchronize()
-        if t0.elapsed_time(t1) >= 1.0:
-            break
-        ctx.check()
-    else:
-        pytest.skip("producer and consumer streams shared a hardware queue (no overlap)")
+    # the context's stream pair runs the combine concurrently with the producer
+    sp, sc = ctx.streams()
+    O = _out(H, D, "f32")
+    ctx.produce(do, dl, schedule=(order, offs), stream=sp)
+    ctx.run_fused(O, stream=sc)
+    torch.cuda.synchronize()
     with pytest.raises(AgemmError) as ei:
         ctx.check()
     assert ei.value.status == ETIMEOUT

@@ -61,7 +61,7 @@ def test_full_size(name, weight):
         for k, v in expect.items():
             assert info[k] == v, (k, info)
     sched = synth.schedule(0x5005, ctx.t, 20_000) if scheduled else None
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     Cf = gu.empty_c(M, N, "f16")
     ctx.produce(dsh, schedule=sched, stream=sp)
     ctx.run_fused(B, Cf, stream=sc)

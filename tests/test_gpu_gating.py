@@ -39,7 +39,7 @@ def test_poisoned_inbox_is_never_read_early(W, M, K, N, gate_mode):
     ctx.produce(nan)  # epochs alternate between two inboxes: poison both
     torch.cuda.synchronize()
     order, offs = synth.schedule(0x5100 + M, ctx.t, 40_000)  # up to 40 us between releases
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     C = gu.empty_c(M, N, "f32")
     ctx.produce(dsh, schedule=(order, offs), stream=sp)
     ctx.run_fused(B, C, stream=sc)
@@ -72,7 +72,7 @@ def test_sixty_four_flags_out_of_order(W, M, K, N, bkf):
     ctx.produce(nan)
     torch.cuda.synchronize()
     order, offs = synth.schedule(0x5300 + M, ctx.t, 10_000)
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     C = gu.empty_c(M, N, "f32")
     ctx.produce(dsh, schedule=(order, offs), stream=sp)
     ctx.run_fused(B, C, stream=sc)
@@ -93,7 +93,7 @@ def test_alternating_epochs(M, gate_mode):
     probs = [gu.random_problem(W, M, K, N, seed=s) for s in (51, 52, 53)]
     refs = [oracle.sharded_gemm(p[1], p[2]) for p in probs]
     ctx = _ctx(W, M, K, N, "f32")
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     outs = []
     for e in range(6):
         p = probs[e % 3]
@@ -123,24 +123,13 @@ def test_timeout_reports_and_recovers(M):
     order = np.arange(ctx.t, dtype=np.int32)
     offs = np.zeros(ctx.t, dtype=np.int64)
     offs[-1] = 30_000_000  # last tile 30 ms late
-    sp = torch.cuda.Stream()
-    for _ in range(4):
-        # HIP maps streams onto a few hardware queues; when the consumer's stream
-        # shares the producer's queue, the consumer runs after every tile is out and
-        # there is nothing to time out on (a correct run): then try a fresh stream.
-        sc = torch.cuda.Stream()
-        C = gu.empty_c(M, N, "f32")
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ctx.produce(dsh, schedule=(order, offs), stream=sp)
-        t0.record(sc)
-        ctx.run_fused(B, C, stream=sc)
-        t1.record(sc)
-        torch.cuda.synchronize()
-        if t0.elapsed_time(t1) >= 1.0:
-            break
-        ctx.check()
-    else:
-        pytest.skip("producer and consumer streams shared a hardware queue (no overlap)")
+    # the context's stream pair runs the consumer concurrently with the producer, so
+    # the consumer is waiting when the late tile's deadline passes
+    sp, sc = ctx.streams()
+    C = gu.empty_c(M, N, "f32")
+    ctx.produce(dsh, schedule=(order, offs), stream=sp)
+    ctx.run_fused(B, C, stream=sc)
+    torch.cuda.synchronize()
     with pytest.raises(AgemmError) as ei:
         ctx.check()
     assert ei.value.status == ETIMEOUT
@@ -203,7 +192,7 @@ def test_flag_tiles_above_31_wait_when_tile_31_is_up(split, monkeypatch):
     order = np.array([31] + list(range(31)) + list(range(32, 64)), dtype=np.int32)
     offs = np.array([0] * 32 + [2_000_000 + 1_000 * i for i in range(32)], dtype=np.int64)
     nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     for _ in range(3):
         ctx.produce(nan)
         ctx.produce(nan)
@@ -237,7 +226,7 @@ def test_epoch_stress_bitwise(M, epochs, gate_mode):
     torch.cuda.synchronize()
     ref0 = oracle.sharded_gemm(probs[0][1], probs[0][2])
     assert np.abs(gu.c_to_f64(refs[0]) - ref0).max() <= oracle.tolerance(K)
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     outs = [gu.empty_c(M, N, "f16") for _ in range(4)]
     bad = []
     for e in range(epochs):
@@ -254,3 +243,28 @@ def test_epoch_stress_bitwise(M, epochs, gate_mode):
     torch.cuda.synchronize()
     ctx.check()
     assert not bad, f"epochs with a result different from their own data: {bad}"
+
+
+def test_stream_pair_runs_producer_and_consumer_concurrently():
+    """agemm_streams: the consumer launched second must start while the producer still
+    waits to release its last tile (2 ms late), so its own kernel time spans the wait;
+    the same pair comes back on later calls."""
+    import torch
+    W, M, K, N = 8, 300, 2048, 1000
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=91)
+    ctx = _ctx(W, M, K, N, "f32")
+    sp, sc = ctx.streams()
+    assert ctx.streams() == (sp, sc)
+    order = np.arange(ctx.t, dtype=np.int32)
+    offs = np.zeros(ctx.t, dtype=np.int64)
+    offs[-1] = 2_000_000
+    C = gu.empty_c(M, N, "f32")
+    ctx.timing_begin(1)
+    ctx.produce(dsh, schedule=(order, offs), stream=sp)
+    ctx.run_fused(B, C, stream=sc)
+    torch.cuda.synchronize()
+    (us,) = ctx.timing_end()
+    ctx.check()
+    assert us >= 1500.0, f"consumer ran {us:.0f} us: it did not overlap the producer"
+    assert np.abs(gu.c_to_f64(C) - oracle.sharded_gemm(sh, b)).max() <= oracle.tolerance(K)
+    ctx.close()

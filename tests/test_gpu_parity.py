@@ -23,7 +23,7 @@ def _ctx(W, M, K, N, c_dtype, **kw):
 def _run(ctx, path, shards, B, C, schedule=None):
     import torch
     if path == "fused":
-        sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+        sp, sc = ctx.streams()
         ctx.produce(shards, schedule=schedule, stream=sp)
         ctx.run_fused(B, C, stream=sc)
     elif path == "fused_preset":

@@ -27,7 +27,7 @@ def _ctx(W, M, K, N, c_dtype="f32"):
 def _paths(ctx, dsh, B, c_dtype, schedule):
     import torch
     out = {}
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     C = gu.empty_c(ctx.M, ctx.N, c_dtype)
     ctx.produce(dsh, schedule=schedule, stream=sp)
     ctx.run_fused(B, C, stream=sc)
@@ -136,7 +136,7 @@ def test_split_back_to_back_calls_reuse_counters(monkeypatch):
         refs.append(C)
     torch.cuda.synchronize()
     assert np.abs(gu.c_to_f64(refs[0]) - oracle.sharded_gemm(probs[0][1], probs[0][2])).max() <= oracle.tolerance(K)
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     bad = []
     for i in range(40):
         p = probs[i % 2]
@@ -177,7 +177,7 @@ def test_arrival_order_on_a_split_context_runs_whole_tiles(monkeypatch):
     ctx.produce(nan)
     ctx.produce(nan)
     torch.cuda.synchronize()
-    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    sp, sc = ctx.streams()
     for order in ("arrival", "shard", "arrival"):
         ctx.set_order(order)
         sched = synth.schedule(0xF900 + len(order), ctx.t, 10_000)

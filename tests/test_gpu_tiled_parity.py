@@ -90,7 +90,7 @@ def _poison(ctx, W, M, K):
 def _run(ctx, path, dsh, B, C, sched):
     import torch
     if path in ("fused", "fused_arrival"):
-        sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+        sp, sc = ctx.streams()
         ctx.produce(dsh, schedule=sched, stream=sp)
         ctx.run_fused(B, C, stream=sc)
     elif path == "bsp":
