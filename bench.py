@@ -140,8 +140,12 @@ def cpu_baseline(W, M, K, N, budget_s: float):
     t0 = time.perf_counter()
     oracle.sharded_gemm(synth.shards(a[:rows], W), b, nthreads=threads)
     t1 = time.perf_counter() - t0
-    if t1 < budget_s / 2 and rows < M:
-        rows = min(M, rows * max(1, int(budget_s / t1)))
+    # grow the sample until it takes at least half the budget (the decode of B is a
+    # fixed cost of every call, so a first estimate undershoots)
+    for _ in range(3):
+        if t1 >= budget_s / 2 or rows >= M:
+            break
+        rows = min(M, rows * max(2, int(budget_s / t1)))
         t0 = time.perf_counter()
         oracle.sharded_gemm(synth.shards(a[:rows], W), b, nthreads=threads)
         t1 = time.perf_counter() - t0
@@ -433,9 +437,11 @@ def main():
     ctx = Context(W, M, K, N, c_dtype=c_dtype)
     ctx.set_order(args.order)
     sched = synth.schedule(0x5005, ctx.t, 20_000) if sched_kind == "random" else None
-    sp, sc = ctx.streams()  # a producer / consumer pair verified to run concurrently
     if args.one_stream:
-        sp = sc
+        # counter collection serialises dispatches, so no pair of streams overlaps there
+        sp = sc = torch.cuda.Stream()
+    else:
+        sp, sc = ctx.streams()  # a producer / consumer pair verified to run concurrently
     torch.cuda.synchronize()
 
     def fused_step(i):

@@ -111,6 +111,7 @@ struct Shape {
   static_assert(CPR_A == 4 || CPR_A == 8, "BK must be 32 or 64");
   static_assert(KSUB == 2 || KSUB == 4, "two or four k-substeps");
   static_assert(LPS * KSUB == LOADS && LPS <= NMF, "loads must spread evenly over the substeps");
+  static_assert(NMF % LPS == 0, "a substep issues its loads one every NMF / LPS MFMAs");
   static_assert(FM <= 4 && FN <= 4, "at most 4x4 MFMA blocks per wave");
 };
 
