@@ -111,7 +111,8 @@ struct Shape {
   static_assert(CPR_A == 4 || CPR_A == 8, "BK must be 32 or 64");
   static_assert(KSUB == 2 || KSUB == 4, "two or four k-substeps");
   static_assert(LPS * KSUB == LOADS && LPS <= NMF, "loads must spread evenly over the substeps");
-  static_assert(NMF % LPS == 0, "a substep issues its loads one every NMF / LPS MFMAs");
+  static constexpr int LSTRIDE = (NMF + LPS - 1) / LPS;  // one direct load every LSTRIDE MFMAs
+  static_assert((LPS - 1) * LSTRIDE < NMF, "a substep issues all its loads between its MFMAs");
   static_assert(FM <= 4 && FN <= 4, "at most 4x4 MFMA blocks per wave");
 };
 
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   static_assert(STAGES >= 2 && STAGES * S::STAGE <= 160 * 1024, "LDS budget");
   static_assert(STAGES * LOADS <= 63, "loads in flight exceed the vmcnt range");
   constexpr int RPM = (NR + NMF / 2 - 1) / (NMF / 2);  // fragment reads after each of the first MFMAs
-  constexpr int LSTRIDE = NMF / LPS;                   // one direct load every LSTRIDE MFMAs
+  constexpr int LSTRIDE = S::LSTRIDE;
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * S::STAGE];
 
@@ -751,7 +752,7 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
     if (gated) { if (out_f32) L(true, true, S_); else L(true, false, S_); }   \
     else { if (out_f32) L(false, true, S_); else L(false, false, S_); }       \
   } while (0)
-  if constexpr (BM == 128 && BN == 128) {
+  if constexpr (BN == 128) {
     if (bnt) {
       if (gated) { if (out_f32) L5(true, true); else L5(true, false); }
       else { if (out_f32) L5(false, true); else L5(false, false); }
@@ -775,18 +776,30 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
 
 }  // namespace
 
-int mfma_config_count() { return 4; }
+int mfma_config_count() { return 5; }
 
+// Default tile by M. Consumer alone, whole tiles, K = 8192, N = 28672, us
+// on MI355X (the stream-K split of the 256x256 tiles measured 202.6 and
+// 206.9 us at M = 224 and 256):
+//   M      128x128 (2)  256x128 (4)  256x256 (0)
+//   128      98.4         131.6        170.0
+//   192     164.5         159.8        181.6
+//   224     173.7         164.7        184.2
+//   256     178.7         169.4        187.6
+//   320     209.8         233.2        210.7
+//   512     325.2         310.3        226.8
+// One row block of 256 covers M up to 256 and reads each element of B once;
+// above that the 256x256 tile moves the fewest bytes per FLOP.
 int mfma_config_for(int64_t M, int tile_config) {
   if (tile_config >= 0 && tile_config < mfma_config_count()) return tile_config;
-  return M > 192 ? 0 : 2;
+  return M <= 128 ? 2 : M <= 256 ? 4 : 0;
 }
 
 MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode) {
   MfmaPlan p;
   p.cfg = mfma_config_for(M, tile_config);
   p.bm = p.cfg == 2 ? 128 : 256;
-  p.bn = p.bm;
+  p.bn = p.cfg == 2 || p.cfg == 4 ? 128 : 256;
   p.tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   // Busiest workgroup's run, in (tile, shard) units: whole tiles dealt to
   // min(tiles, CUs) workgroups, against equal runs of units over min(units, CUs).
@@ -810,7 +823,7 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, in
   // the L2; with few workgroups the nontemporal loads streamed slower (32
   // tiles: 73 against 48 us), so at least half of the CUs must be busy.
   // (Arrival-order launches keep the default policy.)
-  p.bnt = p.cfg == 2 && M <= p.bm && !p.split && 2 * p.grid >= num_cus;
+  p.bnt = p.bn == 128 && M <= p.bm && !p.split && 2 * p.grid >= num_cus;
   if (p.split) {
     p.ws_bytes = sizeof(float) * 2 * (size_t)p.grid * (size_t)(p.bm * p.bn);
     p.cnt_bytes = sizeof(uint32_t) * (size_t)p.tiles;
@@ -826,7 +839,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, cons
     case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 128x128 per wave
     case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, p, out_f32, s, t);   // 8 waves, 128x64 per wave
     case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 64x64 per wave
-    default: return launch_cfg<256, 256, 32, 4, 2, 4>(a, p, out_f32, s, t);  // 8 waves, 128x64, BK 32
+    case 3: return launch_cfg<256, 256, 32, 4, 2, 4>(a, p, out_f32, s, t);   // 8 waves, 128x64, BK 32
+    default: return launch_cfg<256, 128, 32, 4, 2, 2>(a, p, out_f32, s, t);  // 4 waves, 128x64 per wave
   }
 }
 

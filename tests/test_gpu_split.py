@@ -55,14 +55,14 @@ def test_plan(M, N, split):
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     assert ctx.consumer[0] == "mfma"
     assert ctx.split is split
-    bm = 256 if M > 192 else 128
-    tiles = -(-M // bm) * -(-N // bm)
+    info = ctx.consumer_info()
+    tiles = -(-M // info["block_m"]) * -(-N // info["block_n"])
     assert ctx.grid == (min(n_cu, tiles * 8) if split else min(n_cu, tiles))
     ctx.close()
 
 
 @pytest.mark.parametrize("mode", ["0", "1"])
-@pytest.mark.parametrize("tile_config", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile_config", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("W,M,K,N", [
     (8, 300, 2048, 1032),   # 10 tiles x 8 shards: many contributors per tile
     (4, 520, 1024, 264),    # 6 tiles x 4 shards, ragged rows and columns

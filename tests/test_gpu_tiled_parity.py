@@ -38,10 +38,16 @@ CASES = {
     "t256_k1024": (8, 1000, 1024, 16888,
                    dict(kind="mfma", tile_config=0, tiles=264, grid=256, split=0, tiles_per_wg=2,
                         b_nontemporal=0)),
-    # 128x128 tiles: 2 x 160 = 320 tiles, M just over one row block (default B policy)
-    "t128_two_row_blocks": (8, 130, 512, 20480,
-                            dict(kind="mfma", tile_config=2, tiles=320, grid=256, split=0, tiles_per_wg=2,
-                                 b_nontemporal=0)),
+    # 256x128 tiles, one row block (M just over 128, ragged rows): nontemporal B,
+    # 160 workgroups of one tile each
+    "t256x128_nontemporal_b": (8, 130, 512, 20480,
+                               dict(kind="mfma", tile_config=4, tiles=160, grid=160, split=0, tiles_per_wg=1,
+                                    b_nontemporal=1)),
+    # 256x128 tiles, one row block, 300 tiles on 256 workgroups: the cursor crosses
+    # tiles, ragged last columns
+    "t256x128_persistent": (8, 256, 512, 38392,
+                            dict(kind="mfma", tile_config=4, tiles=300, grid=256, split=0, tiles_per_wg=2,
+                                 b_nontemporal=1)),
     # 128x128 tiles, one row block: nontemporal B, 160 workgroups of one tile each
     "t128_nontemporal_b": (8, 96, 1024, 20472,
                            dict(kind="mfma", tile_config=2, tiles=160, grid=160, split=0, tiles_per_wg=1,

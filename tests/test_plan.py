@@ -10,12 +10,20 @@ CUS = 256  # MI355X compute units
 
 
 def _tiles(M, N, cfg):
-    b = 128 if cfg == 2 else 256
-    return -(-M // b) * -(-N // b)
+    bm = 128 if cfg == 2 else 256
+    bn = 128 if cfg in (2, 4) else 256
+    return -(-M // bm) * -(-N // bn)
+
+
+def _default_cfg(M):
+    return 2 if M <= 128 else 4 if M <= 256 else 0
 
 
 @pytest.mark.parametrize("M,N,cfg,grid,split", [
     (128, 28672, 2, 224, False),   # crossover workload: 224 whole 128x128 tiles (split loses here)
+    (256, 28672, 4, 224, False),   # one row block of 256x128 tiles
+    (129, 28672, 4, 224, False),
+    (257, 28672, 0, 224, False),
     (512, 28672, 0, 224, False),   # out-of-order workload: 224 whole 256x256 tiles
     (4096, 28672, 0, 256, False),  # prefill workload: 1792 tiles, 7 per CU
     (128, 4096, 2, 256, True),     # 32 tiles: split over one workgroup per CU
@@ -36,11 +44,11 @@ def test_forced_modes_and_single_shard():
 
 
 def test_plan_invariants_over_a_sweep():
-    for M, N, W, cus, tc, mode in itertools.product((1, 9, 128, 129, 300, 4096), (8, 264, 4096, 28672),
-                                                    (1, 2, 3, 8, 16), (7, 80, 256, 304), (-1, 0, 2),
+    for M, N, W, cus, tc, mode in itertools.product((1, 9, 128, 129, 256, 300, 4096), (8, 264, 4096, 28672),
+                                                    (1, 2, 3, 8, 16), (7, 80, 256, 304), (-1, 0, 2, 4),
                                                     (-1, 0, 1)):
         cfg, grid, split = agemm.mfma_plan(M, N, W, cus, tc, mode)
-        assert cfg == (tc if tc >= 0 else (0 if M > 192 else 2))
+        assert cfg == (tc if tc >= 0 else _default_cfg(M))
         t = _tiles(M, N, cfg)
         if split:
             assert W >= 2 and grid == min(t * W, cus)
@@ -52,7 +60,7 @@ def test_plan_invariants_over_a_sweep():
 
 
 @pytest.mark.parametrize("args", [(0, 64, 8, CUS, -1, -1), (8, 4, 8, CUS, -1, -1), (8, 64, 0, CUS, -1, -1),
-                                  (8, 64, 17, CUS, -1, -1), (8, 64, 8, 0, -1, -1), (8, 64, 8, CUS, 4, -1),
+                                  (8, 64, 17, CUS, -1, -1), (8, 64, 8, 0, -1, -1), (8, 64, 8, CUS, 5, -1),
                                   (8, 64, 8, CUS, -1, 2)])
 def test_plan_rejects_bad_arguments(args):
     with pytest.raises(agemm.AgemmError) as ei:
