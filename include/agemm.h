@@ -156,11 +156,16 @@ int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, i
  *   b_nontemporal  1: B's loads skip L2 allocation (one row block of whole tiles;
  *                  not in arrival order)
  *   tiles_per_wg   most output tiles one workgroup runs (whole tiles), 1 with the split
- *   ranges         small-M K-ranges (0 for MFMA) */
+ *   ranges         small-M K-ranges (0 for MFMA)
+ *   a_panels       1: the inbox and the BSP buffer hold A in 32-column k-panels
+ *                  (each panel M rows of 32 contiguous elements; the MFMA
+ *                  consumer then reads 64-byte rows that lie side by side),
+ *                  0: row-major (small-M, or a flag tile's panels of 2^31 bytes
+ *                  or more) */
 typedef struct {
   int32_t kind, tile_config, block_m, block_n;
   int32_t tiles, grid, split, b_nontemporal;
-  int32_t tiles_per_wg, ranges;
+  int32_t tiles_per_wg, ranges, a_panels;
 } agemm_consumer_desc;
 int agemm_consumer_info(const agemm_ctx* ctx, agemm_consumer_desc* out);
 

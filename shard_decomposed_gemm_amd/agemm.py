@@ -40,7 +40,7 @@ class Schedule(ctypes.Structure):
 class ConsumerDesc(ctypes.Structure):
     """agemm_consumer_desc: the consumer launch a context's calls make."""
     _fields_ = [(n, ctypes.c_int32) for n in ("kind", "tile_config", "block_m", "block_n", "tiles", "grid", "split",
-                                               "b_nontemporal", "tiles_per_wg", "ranges")]
+                                               "b_nontemporal", "tiles_per_wg", "ranges", "a_panels")]
 
 
 _lib = None

@@ -42,6 +42,10 @@ struct agemm_ctx {
   uint64_t* t0_fused = nullptr;
   uint64_t* t0_bsp = nullptr;
   _Float16* gathered = nullptr;  // M x K, BSP only
+  // Layout of the inbox and of the BSP buffer (see ASource): k-panels for the
+  // MFMA consumer where a flag tile's panels stay below 2^31 bytes,
+  // row-major otherwise (the small-M kernel streams rows).
+  int32_t a_panels = 0;
   SmallMPlan small_plan;         // small-M work split (small_plan.ok: the small-M kernel is used)
   float* ws = nullptr;           // small-M split-K workspace, ranges x M x N
   uint32_t* counters = nullptr;  // small-M column-block counters
@@ -103,6 +107,7 @@ void base_produce_args(agemm_ctx* c, const void* const* a_shards, ProduceArgs& p
   pa.t = c->t;
   pa.rows_per_item = c->rows_per_item;
   pa.items_per_tile = c->items_per_tile;
+  pa.panels = c->a_panels;
 }
 
 // Orders a new consumer after the previous consumer call of the context.
@@ -267,6 +272,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     }
   }
   const bool small = c->small_plan.ok;
+  c->a_panels = !small && panel_layout_fits(M, bkf) ? 1 : 0;
   if (!small) {
     int split_mode = -1;
     if (const char* env = std::getenv("AGEMM_SPLIT")) split_mode = std::atoi(env) != 0 ? 1 : 0;
@@ -378,6 +384,7 @@ int agemm_consumer_info(const agemm_ctx* ctx, agemm_consumer_desc* out) {
     d.split = q.split ? 1 : 0;
     d.b_nontemporal = q.bnt && !arrival ? 1 : 0;
     d.tiles_per_wg = q.split ? 1 : (int32_t)((q.tiles + q.grid - 1) / q.grid);
+    d.a_panels = ctx->a_panels;
   }
   *out = d;
   return AGEMM_OK;
@@ -469,6 +476,7 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   for (int i = 0; i < kMaxShards; ++i)
     src.base[i] = i < ctx->W ? ctx->inbox[slot] + (int64_t)i * ctx->M * ctx->KS : nullptr;
   src.lda = ctx->KS;
+  src.panels = ctx->a_panels;
   Gate gate = no_gate(ctx);
   gate.flags = ctx->flags[slot];
   gate.target = ctx->slot_epochs[slot] * (uint32_t)ctx->items_per_tile;  // wraps with the counters
@@ -494,9 +502,10 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   rc = order_after_consumer(ctx, s);
   if (rc) return rc;
   // 1) all-gather stand-in: copy the shards into one M x K buffer
+  // ([A_0 | ... | A_{W-1}] row-major, or shard after shard in k-panels)
   base_produce_args(ctx, a_shards, pa);
   pa.dst = ctx->gathered;
-  pa.dst_shard_stride = ctx->KS;
+  pa.dst_shard_stride = ctx->a_panels ? ctx->M * ctx->KS : ctx->KS;
   pa.dst_ld = ctx->K;
   pa.flags = nullptr;
   pa.t0 = ctx->t0_bsp;
@@ -511,8 +520,9 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   }
   // 3) the same GEMM with the flags off, reading the gathered A
   ASource src{};
-  for (int i = 0; i < kMaxShards; ++i) src.base[i] = i < ctx->W ? ctx->gathered + (int64_t)i * ctx->KS : nullptr;
+  for (int i = 0; i < kMaxShards; ++i) src.base[i] = i < ctx->W ? ctx->gathered + (int64_t)i * pa.dst_shard_stride : nullptr;
   src.lda = ctx->K;
+  src.panels = ctx->a_panels;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
   const hipError_t eo = ctx->so.after_other(s);

@@ -18,11 +18,29 @@ struct ErrWord {
   uint32_t seen;     // last flag value observed
 };
 
-// Where the GEMM reads its A operand for shard s: a_base[s] + m * lda + j.
+// Columns of one k-panel of the inbox layout (see ASource).
+constexpr int kPanelK = 32;
+
+// Where the GEMM reads its A operand for shard s. Row-major (panels == 0):
+// element (m, j) at base[s] + m * lda + j. K-panels (panels == 1): the shard
+// is cut into panels of kPanelK columns, each stored as M rows of kPanelK
+// contiguous elements, one panel after the other: element (m, j) at
+// base[s] + ((j / kPanelK) * M + m) * kPanelK + j % kPanelK. A tile's k-step
+// then reads whole contiguous rows of 64 bytes that sit next to each other,
+// instead of 64-byte pieces one row apart; the producer and the gather copy
+// write this layout into the inbox and the BSP buffer.
 struct ASource {
   const _Float16* base[kMaxShards];
   int64_t lda;
+  int32_t panels;
 };
+
+// The k-panel layout addresses a flag tile's panels with 32-bit byte offsets
+// (buffer stores and lane offsets): it is used when BKf / kPanelK panels of
+// M rows stay below 2^31 bytes.
+inline bool panel_layout_fits(int64_t M, int64_t bkf) {
+  return bkf % kPanelK == 0 && (bkf / kPanelK) * M * (kPanelK * 2) < (int64_t{1} << 31);
+}
 
 // Flag gate of the consumer. flags == nullptr disables gating.
 struct Gate {
@@ -89,8 +107,9 @@ struct MfmaPlan {
 struct ProduceArgs {
   const _Float16* src[kMaxShards];  // A_s, M x KS
   _Float16* dst;                    // inbox base or gathered A
-  int64_t dst_shard_stride;         // elements between shard slots (inbox: M*KS; gather: KS)
-  int64_t dst_ld;                   // row stride of dst (inbox: KS; gather: K)
+  int32_t panels;                   // 1: dst in the k-panel layout of ASource (dst_ld unused)
+  int64_t dst_shard_stride;         // elements between shard slots (inbox, panels: M*KS; row-major gather: KS)
+  int64_t dst_ld;                   // row stride of a row-major dst (inbox: KS; gather: K)
   uint32_t* flags;                  // nullptr in gather mode
   uint64_t* t0;                     // device, 2 words: common start time per launch parity
   uint32_t parity;

@@ -266,6 +266,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   int64_t a_row0 = 0;
   uint32_t a_off[S::A_ITERS], b_off[S::B_ITERS];
   const int64_t lda2 = g.a.lda * 2;
+  // A's byte step from one k-step to the next: BK columns of a row-major
+  // shard, or BK / 32 whole panels of the k-panel layout.
+  const bool panels = g.a.panels != 0;
+  const int64_t panel_bytes = M * (kPanelK * 2);
+  const int64_t a_kstep = panels ? (int64_t)(BK / kPanelK) * panel_bytes : (int64_t)BK * 2;
 
   // Flag gate of the tile the cursor enters (called from cursor_enter and at
   // each flag-tile crossing of cursor_advance, before any load of the tile).
@@ -370,11 +375,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     tile_coords(cseg.w, m0, n0);
     const int rmax = (int)(M - 1 - m0);
 #pragma unroll
-    for (int j = 0; j < S::A_ITERS; ++j) a_off[j] = sched::a_src_offset<BK>(j * NT + wave * 64 + lane, rmax, lda2);
+    for (int j = 0; j < S::A_ITERS; ++j) {
+      const int q = j * NT + wave * 64 + lane;
+      a_off[j] = panels ? sched::a_src_offset_panels<BK>(q, rmax, panel_bytes) : sched::a_src_offset<BK>(q, rmax, lda2);
+    }
     const int cmax = (int)(N - 8 - n0);
 #pragma unroll
     for (int j = 0; j < S::B_ITERS; ++j) b_off[j] = sched::b_src_offset<BN>(j * NT + wave * 64 + lane, cmax, N);
-    a_row0 = m0 * lda2;
+    a_row0 = panels ? m0 * (kPanelK * 2) : m0 * lda2;
     if constexpr (ARRIVAL) {
       c_n0 = n0;
       ct = 0;
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     taken |= 1ull << f;
     const int fs = f / g.gate.kt;
     const int step = sched::flag_first_step(f, g.gate.kt, SPS, spt);
-    ca = (const char*)g.a.base[fs] + a_row0 + (int64_t)(step - fs * SPS) * BK * 2;
+    ca = (const char*)g.a.base[fs] + a_row0 + (int64_t)(step - fs * SPS) * a_kstep;
     cb = (const char*)g.B + c_n0 * 2 + (int64_t)step * BK * N * 2;
     gate(f);
   };
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
       if (seg_next(cseg)) {
         cursor_enter();
       } else {
-        ca -= BK * 2;
+        ca -= a_kstep;
         cb -= (int64_t)BK * N * 2;
         kp.ct = cseg.ke - 1;
       }
@@ -443,11 +451,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
         choose();
       } else {
         cb += (int64_t)BK * N * 2;
-        ca += BK * 2;
+        ca += a_kstep;
       }
       return;
     }
-    ca += BK * 2;
+    ca += a_kstep;
     cb += (int64_t)BK * N * 2;
     if (__builtin_expect(sched::kpos_step(kp, cseg.ke), 0)) cursor_event();
   };

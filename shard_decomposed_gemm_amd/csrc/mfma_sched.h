@@ -238,6 +238,18 @@ AGEMM_HD uint32_t a_src_offset(int q, int rmax, int64_t lda_bytes) {
   return (uint32_t)(r * lda_bytes + c * 16);
 }
 
+// The same chunk in the k-panel layout (32-column panels of M rows of 64
+// bytes, panel_bytes = M * 64 apart): byte offset from the k-step's first
+// panel at the tile's first row. BK = 64 spans two panels.
+template <int BK>
+AGEMM_HD uint32_t a_src_offset_panels(int q, int rmax, int64_t panel_bytes) {
+  constexpr int CPR = BK / 8;
+  int r = q / CPR;
+  const int c = (q % CPR) ^ swz_a<CPR>(r);
+  r = r < rmax ? r : rmax;
+  return (uint32_t)((c >> 2) * panel_bytes + r * 64 + (c & 3) * 16);
+}
+
 // Chunk q of a stage's B block (BK rows x BN columns): byte offset of its
 // source from the k-step's first row at the tile's first column, columns past
 // N clamped to the last 8 (their results are never stored).

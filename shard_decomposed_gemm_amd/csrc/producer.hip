@@ -78,18 +78,43 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
     const int cpr = a.bkf >> 3;  // 16-byte chunks per row segment
     const int64_t total = (r1 - r0) * cpr;
     const _Float16* __restrict__ src = a.src[s] + (int64_t)kt * a.bkf;
-    _Float16* __restrict__ dst = a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * a.bkf + r0 * a.dst_ld;
-    // Push: the item's rows of its inbox slot, (r1 - r0 - 1) * KS + bkf elements
-    // (under 64 MiB: an item holds at most 1 MiB of a tile, and KS / bkf <= 64).
-    // (The gather copy stores plainly and leaves the descriptor empty.)
-    const int span = FLAGS ? (int)(((r1 - r0 - 1) * a.dst_ld + a.bkf) * 2) : 0;
+    // Row-major dst: the item's rows of the tile's columns. K-panel dst: the
+    // item's rows of each of the tile's bkf / 32 panels (panel_ld = M * 32
+    // elements apart), chunks taken panel by panel so that a wave's stores
+    // are contiguous.
+    const int64_t panel_ld = a.M * kPanelK;
+    const int rows = (int)(r1 - r0);
+    _Float16* __restrict__ dst =
+        a.panels ? a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * (a.bkf / kPanelK) * panel_ld + r0 * kPanelK
+                 : a.dst + (int64_t)s * a.dst_shard_stride + (int64_t)kt * a.bkf + r0 * a.dst_ld;
+    // Push: the byte range the item's stores fall in, under 2^31 (row-major:
+    // an item holds at most 1 MiB of a tile and KS / bkf <= 64; k-panels: the
+    // context uses them only where a tile's panels span less). The gather
+    // copy stores plainly and leaves the descriptor empty.
+    const int span = !FLAGS ? 0
+                     : a.panels ? (int)(((a.bkf / kPanelK - 1) * panel_ld + rows * kPanelK) * 2)
+                                : (int)(((r1 - r0 - 1) * a.dst_ld + a.bkf) * 2);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, span, kRsrcWord3);
 
     // Four 16-byte chunks in flight per thread (plain registers, no arrays).
+    // Chunk cc: row-major (row cc / cpr, chunk cc % cpr); k-panels (panel
+    // cc / (4 rows), row, chunk cc % 4 of the panel row).
     auto src_at = [&](int64_t cc) {
+      if (a.panels) {
+        const int ci = (int)cc, per_panel = rows * 4;
+        const int p = ci / per_panel, rem = ci - p * per_panel;
+        return reinterpret_cast<const uint4*>(src + (r0 + (rem >> 2)) * a.KS + p * kPanelK + (rem & 3) * 8);
+      }
       return reinterpret_cast<const uint4*>(src + (r0 + cc / cpr) * a.KS + (cc % cpr) * 8);
     };
-    auto dst_off = [&](int64_t cc) { return (cc / cpr) * a.dst_ld + (cc % cpr) * 8; };  // elements
+    auto dst_off = [&](int64_t cc) -> int64_t {  // elements
+      if (a.panels) {
+        const int ci = (int)cc, per_panel = rows * 4;
+        const int p = ci / per_panel, rem = ci - p * per_panel;
+        return p * panel_ld + rem * 8;
+      }
+      return (cc / cpr) * a.dst_ld + (cc % cpr) * 8;
+    };
     auto put = [&](int64_t cc, const uint4& v) {
       if constexpr (FLAGS) {
         const u32x4 x = {v.x, v.y, v.z, v.w};

@@ -9,7 +9,8 @@
 //   - the cursor loads exactly the step the compute walk consumes from that
 //     buffer: right tile, right shard buffer, right column and B rows;
 //   - every 16-byte lane load lies inside its shard buffer (inbox or source
-//     shards, and the BSP gather buffer) and inside B, and a stage's chunks
+//     shards, and the BSP gather buffer; row-major and in 32-column k-panels)
+//     and inside B, reads the element it stands for, and a stage's chunks
 //     cover each (row, chunk) of the tile exactly once (swizzle bijective);
 //   - gated launches: a flag tile is gated before any load from it, under
 //     three models of what a flag poll reveals (only the awaited tile, all,
@@ -78,24 +79,35 @@ bool check_lane_loads(const Shape& s, int w, const Load& L, const TileGrid& tg) 
   const int rmax = (int)(s.M - 1 - m0);
   const int cmax = (int)(s.N - 8 - n0);
   const int64_t K = (int64_t)s.W * s.KS;
-  // two A layouts: shard buffers (lda = KS) and the BSP gather buffer (lda = K)
-  for (int gathered = 0; gathered < 2; ++gathered) {
+  // four A layouts: row-major shard buffers (lda = KS) and BSP gather buffer
+  // (lda = K); the k-panel layout of the inbox and of the gather buffer
+  // (32-column panels of M rows of 64 bytes, shard after shard)
+  for (int layout = 0; layout < 4; ++layout) {
+    const bool gathered = layout & 1, panels = layout >= 2;
     const int64_t lda = gathered ? K : s.KS;
-    const int64_t base = gathered ? (int64_t)L.shard * s.KS * 2 : 0;
+    const int64_t base = !gathered ? 0 : panels ? (int64_t)L.shard * s.M * s.KS * 2 : (int64_t)L.shard * s.KS * 2;
     const int64_t buf_bytes = gathered ? s.M * K * 2 : s.M * s.KS * 2;
+    const int64_t pb = s.M * 64;  // bytes of one panel
     const int cpr = c.BK / 8;
     std::vector<int> seen((size_t)c.BM * cpr, 0);
     for (int q = 0; q < c.BM * cpr; ++q) {
-      const uint32_t off = c.BK == 32 ? a_src_offset<32>(q, rmax, lda * 2) : a_src_offset<64>(q, rmax, lda * 2);
-      const int64_t addr = base + m0 * lda * 2 + L.a_col * 2 + off;
-      CHECK(addr >= 0 && addr + 16 <= buf_bytes, "A load out of bounds: tile %d step %d q %d addr %lld size %lld", w,
-            L.ct, q, (long long)addr, (long long)buf_bytes);
+      uint32_t off;
+      if (panels) off = c.BK == 32 ? a_src_offset_panels<32>(q, rmax, pb) : a_src_offset_panels<64>(q, rmax, pb);
+      else off = c.BK == 32 ? a_src_offset<32>(q, rmax, lda * 2) : a_src_offset<64>(q, rmax, lda * 2);
+      // the kernel's cursor: tile's first row, plus one k-step's bytes per step
+      const int64_t cursor = panels ? base + m0 * 64 + (L.a_col / 32) * pb : base + m0 * lda * 2 + L.a_col * 2;
+      const int64_t addr = cursor + off;
+      CHECK(addr >= 0 && addr + 16 <= buf_bytes,
+            "A load out of bounds: layout %d tile %d step %d q %d addr %lld size %lld", layout, w, L.ct, q,
+            (long long)addr, (long long)buf_bytes);
       const int r = q / cpr;
       const int ch = (q % cpr) ^ (c.BK == 32 ? swz_a<4>(r) : swz_a<8>(r));
       CHECK(ch >= 0 && ch < cpr, "A swizzled chunk out of range");
       if (r <= rmax) {  // rows past M are clamped and never stored
-        CHECK(addr == base + (m0 + r) * lda * 2 + L.a_col * 2 + ch * 16, "A chunk %d of row %d at the wrong source", ch,
-              r);
+        const int64_t col = L.a_col + ch * 8;  // element column inside the shard
+        const int64_t want = panels ? base + ((col / 32) * s.M + m0 + r) * 64 + (col % 32) * 2
+                                    : base + (m0 + r) * lda * 2 + col * 2;
+        CHECK(addr == want, "A chunk %d of row %d at the wrong source (layout %d)", ch, r, layout);
         seen[(size_t)r * cpr + ch]++;
       }
     }
