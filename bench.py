@@ -388,7 +388,7 @@ def main():
     ap.add_argument("--sweep", default=None,
                     help="comma-separated M values at K=8192, N=28672, W=8: the fused / BSP / Pull ladder "
                          "per M (one JSON object per M, then a markdown table); no headline line")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline (the timed sample takes 10 to 20 s)")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps, so the engine clock has settled")
     ap.add_argument("--order", choices=["shard", "arrival"], default="shard",

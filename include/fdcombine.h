@@ -68,8 +68,11 @@ int fdc_tiles(const fdc_ctx* ctx, int32_t* t);
  * (sched == NULL: tile order, no delay), copies rank s's rows of head tile j
  * (outputs and statistics) into Inbox(s, j) with device-coherent stores,
  * then raises Flags(s, j). o_parts and lse_parts: host arrays of W device
- * pointers. Starts a new epoch; the producer stream waits (device side) for
- * the fused combine that last read the same inbox, two epochs before. */
+ * pointers. Starts a new epoch. Its kernel first waits on the device until
+ * every fused combine issued so far on the same inbox (the epochs two, four,
+ * ... before) has finished reading it: each head wave of a combine counts
+ * itself in after its last read (the inbox guard; no stream dependency on
+ * the combines). Producer calls stay ordered among themselves. */
 int fdc_produce(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse_parts,
                 const agemm_schedule* sched, void* stream);
 
@@ -85,7 +88,8 @@ int fdc_run_fused(fdc_ctx* ctx, void* O, void* stream);
 int fdc_run_bsp(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse_parts, void* O,
                 const agemm_schedule* sched, int host_sync, void* stream);
 
-/* Spin timeout of the flag waits in microseconds (default 2,000,000). */
+/* Spin timeout of the flag waits and of the producer's inbox guard, in
+ * microseconds (default 2,000,000). */
 int fdc_set_spin_timeout_us(fdc_ctx* ctx, int64_t us);
 
 /* A producer and a consumer stream, owned by the context, on which kernels
@@ -100,9 +104,9 @@ int fdc_streams(fdc_ctx* ctx, void** producer, void** consumer);
 int fdc_timing_begin(fdc_ctx* ctx, int32_t max_launches);
 int fdc_timing_end(fdc_ctx* ctx, float* us, int32_t max, int32_t* count);
 
-/* AGEMM_ETIMEOUT if a combine gave up waiting since the last check (the error
- * word is then cleared), else AGEMM_OK. Reads host-mapped memory: synchronise
- * the consumer's stream first. */
+/* AGEMM_ETIMEOUT if a combine gave up waiting for a flag, or a producer for
+ * its inbox guard, since the last check (the error word is then cleared),
+ * else AGEMM_OK. Reads host-mapped memory: synchronise both streams first. */
 int fdc_check(fdc_ctx* ctx);
 
 /* Message of the last failed call on this context ("" if none). */

@@ -39,6 +39,30 @@ __global__ __launch_bounds__(kFdThreads) void fd_produce_kernel(FdProduceArgs a)
   const int s = tile / a.L.nht;
   const int j = tile - s * a.L.nht;
 
+  if constexpr (FLAGS) {
+    // Inbox guard: the fused combines that read this inbox before must be
+    // done with it. Their head waves count themselves in after their last
+    // read; the stores below cannot overtake those reads, which had
+    // returned before the count was raised.
+    if (threadIdx.x == 0) {
+      const uint64_t start = fd_clock();
+      while (true) {
+        const uint32_t v = __hip_atomic_load(const_cast<uint32_t*>(a.consumed), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        if ((int32_t)(v - a.consumed_target) >= 0) break;
+        if (fd_clock() - start > a.timeout_ticks) {
+          __hip_atomic_store(&a.err->tile, (uint32_t)tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(&a.err->target, a.consumed_target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(&a.err->seen, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(&a.err->code, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    __syncthreads();
+  }
+
   if (a.has_delay) {
     // The first workgroup of the launch fixes its start time; launches with a
     // schedule alternate between two start slots, each clearing the other.
@@ -166,6 +190,12 @@ __global__ __launch_bounds__(kFdThreads) void fd_combine_kernel(FdCombineArgs a)
     _Float16* out = static_cast<_Float16*>(a.O) + (int64_t)h * a.L.D;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = (_Float16)(acc[k] * inv);
+  }
+  if constexpr (GATED) {
+    // This head's reads of the inbox have all returned: count it in, so that
+    // a later producer of this inbox may overwrite it.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(a.consumed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -27,6 +27,15 @@ struct FdProduceArgs {
   int32_t has_delay;
   int32_t order[kMaxTiles];          // tile released p-th
   uint32_t offset_ticks[kMaxTiles];  // its release time after the launch's start
+  // Inbox guard (push only): before writing, every workgroup waits until
+  // *consumed has reached consumed_target, the count of head waves of every
+  // fused combine issued on this inbox so far (each counts itself in once it
+  // has read its last block). Bounded by timeout_ticks; a timeout is
+  // recorded in *err with code 2.
+  const uint32_t* consumed;
+  uint32_t consumed_target;
+  uint64_t timeout_ticks;
+  ErrWord* err;
 };
 
 struct FdCombineArgs {
@@ -37,6 +46,7 @@ struct FdCombineArgs {
   uint32_t target;         // flag value that means "this epoch's tile is in"
   uint64_t timeout_ticks;  // wall-clock ticks
   ErrWord* err;
+  uint32_t* consumed;      // gated: the inbox's consumed count, +1 per head wave when it is done reading
 };
 
 hipError_t launch_fd_produce(const FdProduceArgs& a, hipStream_t s);

@@ -110,6 +110,11 @@ hipError_t StreamOrder::before_produce(int slot, hipStream_t s) {
   return e;
 }
 
+hipError_t StreamOrder::after_last_producer(hipStream_t s) {
+  if (producer_pending && producer_stream != s) return hipStreamWaitEvent(s, ev_producer, 0);
+  return hipSuccess;
+}
+
 hipError_t StreamOrder::after_produce(hipStream_t s) {
   const hipError_t e = hipEventRecord(ev_producer, s);
   if (e == hipSuccess) {

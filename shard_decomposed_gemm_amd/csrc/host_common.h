@@ -49,6 +49,9 @@ struct StreamOrder {
   hipError_t create();
   void destroy();
   hipError_t before_produce(int slot, hipStream_t s);
+  // Only the producer-after-producer order of before_produce (for a context
+  // whose producer guards its inbox on the device).
+  hipError_t after_last_producer(hipStream_t s);
   hipError_t after_produce(hipStream_t s);
   hipError_t before_consumer(hipStream_t s);
   hipError_t after_fused(int slot, hipStream_t s);

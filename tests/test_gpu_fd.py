@@ -165,6 +165,35 @@ def test_fd_alternating_epochs():
         assert np.abs(O.cpu().numpy().astype(np.float64) - refs[e % 3]).max() <= fdo.tolerance("f32"), e
 
 
+def test_fd_inbox_guard_holds_the_producer_for_a_late_combine():
+    """The combine of epoch 0 starts late (its stream first runs a long matrix product),
+    after the producers of epochs 1 and 2 were issued. Epoch 2 reuses epoch 0's inbox:
+    its producer must wait on the device until that combine has read it, so every
+    epoch's output still matches its own partials."""
+    import torch
+    W, H, D, HT = 8, 96, 128, 16
+    sets = [synth.fd_partials(0x7B00 + 16 * k, W, H, D) for k in range(3)]
+    refs = [fdo.combine(o, l) for o, l in sets]
+    devs = [_dev_parts(o, l) for o, l in sets]
+    ctx = _ctx(W, H, D, HT, "f32")
+    sp, sc = ctx.streams()
+    x = torch.full((8192, 8192), 1e-4, device=gu.dev())
+    torch.cuda.synchronize()
+    outs = []
+    with torch.cuda.stream(sc):
+        y = x @ x  # several milliseconds ahead of the first combine on its stream
+    for k in range(3):
+        O = _out(H, D, "f32")
+        ctx.produce(*devs[k], stream=sp)
+        ctx.run_fused(O, stream=sc)
+        outs.append(O)
+    torch.cuda.synchronize()
+    ctx.check()
+    assert torch.isfinite(y).all()
+    for k, O in enumerate(outs):
+        assert np.abs(O.cpu().numpy().astype(np.float64) - refs[k]).max() <= fdo.tolerance("f32"), k
+
+
 def test_fd_timeout_reports_and_recovers():
     """A tile released long after the spin timeout: the combine stops waiting, fdc_check
     reports ETIMEOUT, and the next epoch is correct again."""
