@@ -107,10 +107,9 @@ typedef struct {
  * this call (all optional; invalid values are ignored):
  *   AGEMM_SPIN_TIMEOUT_MS    consumer flag-wait timeout (default 2000 ms)
  *   AGEMM_STRICT_ACQUIRE=1   agent-scope acquire fence after each flag wait
- *   AGEMM_TILE_CONFIG=0..4   MFMA tile configuration, BM x BN (waves, BK): 0 256x256
- *                            (4, 32), 1 256x256 (8, 64), 2 128x128 (4, 64),
- *                            3 256x256 (8, 32), 4 256x128 (4, 32). Default: 2 for
- *                            M <= 128, 4 for M <= 256, else 0
+ *   AGEMM_TILE_CONFIG=0..2   MFMA tile configuration, BM x BN (four waves, BK): 0
+ *                            256x256 (BK 32), 1 128x128 (BK 64), 2 256x128 (BK 32).
+ *                            Default: 1 for M <= 128, 2 for M <= 256, else 0
  *   AGEMM_SPLIT=0|1          MFMA work split: 0 whole tiles only, 1 the stream-K
  *                            split whenever W >= 2 (default: the split when whole
  *                            tiles would leave at least half of the CUs idle)
@@ -127,14 +126,14 @@ int agemm_destroy(agemm_ctx* ctx);
 int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
 
 /* Consumer kernel the context's GEMM calls launch: *kind = 0 for the MFMA
- * tile kernel (then *tile_config is its tile configuration, 0..4), 1 for the
+ * tile kernel (then *tile_config is its tile configuration, 0..2), 1 for the
  * small-M split-K streaming kernel (M <= 8; *tile_config = -1). Either output
  * pointer may be NULL. */
 int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_config);
 
 /* The MFMA consumer's work plan for a shape on a GPU with num_cus compute
  * units, computed on the host without a device (the choice agemm_create
- * makes): *cfg = tile configuration 0..4, *grid = workgroups of the
+ * makes): *cfg = tile configuration 0..2, *grid = workgroups of the
  * persistent grid, *split = 1 for the stream-K split. tile_config -1 and
  * split_mode -1 are the automatic choices (AGEMM_TILE_CONFIG / AGEMM_SPLIT
  * give the others). Applies to the MFMA consumer only (a context with
@@ -147,7 +146,7 @@ int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, i
 /* Everything the context's consumer launches are built from (fixed at create
  * time, except where the order set by agemm_set_order changes it, as noted).
  *   kind           0: MFMA tile kernel, 1: small-M split-K streaming kernel
- *   tile_config    MFMA tile configuration 0..4 (-1 for small-M)
+ *   tile_config    MFMA tile configuration 0..2 (-1 for small-M)
  *   block_m/_n     output tile of one MFMA workgroup (0 for small-M)
  *   tiles          output tiles (MFMA) or work items (small-M: K-ranges x column blocks)
  *   grid           workgroups of the launch (a persistent grid: at most one MFMA

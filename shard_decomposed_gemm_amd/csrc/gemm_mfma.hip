@@ -784,12 +784,12 @@ hipError_t launch_cfg(const GemmArgs& a, const MfmaPlan& p, bool out_f32, hipStr
 
 }  // namespace
 
-int mfma_config_count() { return 5; }
+int mfma_config_count() { return 3; }
 
 // Default tile by M. Consumer alone, whole tiles, K = 8192, N = 28672, us
 // on MI355X (the stream-K split of the 256x256 tiles measured 202.6 and
 // 206.9 us at M = 224 and 256):
-//   M      128x128 (2)  256x128 (4)  256x256 (0)
+//   M      128x128 (1)  256x128 (2)  256x256 (0)
 //   128      98.4         131.6        170.0
 //   192     164.5         159.8        181.6
 //   224     173.7         164.7        184.2
@@ -800,14 +800,14 @@ int mfma_config_count() { return 5; }
 // above that the 256x256 tile moves the fewest bytes per FLOP.
 int mfma_config_for(int64_t M, int tile_config) {
   if (tile_config >= 0 && tile_config < mfma_config_count()) return tile_config;
-  return M <= 128 ? 2 : M <= 256 ? 4 : 0;
+  return M <= 128 ? 1 : M <= 256 ? 2 : 0;
 }
 
 MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode) {
   MfmaPlan p;
   p.cfg = mfma_config_for(M, tile_config);
-  p.bm = p.cfg == 2 ? 128 : 256;
-  p.bn = p.cfg == 2 || p.cfg == 4 ? 128 : 256;
+  p.bm = p.cfg == 1 ? 128 : 256;
+  p.bn = p.cfg == 0 ? 256 : 128;
   p.tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   // Busiest workgroup's run, in (tile, shard) units: whole tiles dealt to
   // min(tiles, CUs) workgroups, against equal runs of units over min(units, CUs).
@@ -845,9 +845,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, cons
   if (p.split && (!a.split_ws || !a.split_cnt)) return hipErrorInvalidValue;
   switch (p.cfg) {
     case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 128x128 per wave
-    case 1: return launch_cfg<256, 256, 64, 2, 2, 4>(a, p, out_f32, s, t);   // 8 waves, 128x64 per wave
-    case 2: return launch_cfg<128, 128, 64, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 64x64 per wave
-    case 3: return launch_cfg<256, 256, 32, 4, 2, 4>(a, p, out_f32, s, t);   // 8 waves, 128x64, BK 32
+    case 1: return launch_cfg<128, 128, 64, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 64x64 per wave
     default: return launch_cfg<256, 128, 32, 4, 2, 2>(a, p, out_f32, s, t);  // 4 waves, 128x64 per wave
   }
 }

@@ -53,7 +53,7 @@ def _fused_concurrent(ctx, dsh, B, C, schedule):
     ctx.check()
 
 
-@pytest.mark.parametrize("tile_config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile_config", [0, 1, 2])
 @pytest.mark.parametrize("W,M,K,N", [(8, 300, 2048, 1032), (4, 520, 1024, 264), (16, 257, 1024, 264)])
 def test_arrival_exact_inputs_bitwise(tile_config, W, M, K, N, monkeypatch):
     """Exact inputs (every partial sum exact in fp32): whatever order the tiles arrive

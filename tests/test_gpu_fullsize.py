@@ -23,7 +23,7 @@ W, K, N = 8, 8192, 28672
 CONFIGS = {
     # name: (M, schedule?, flag-tile order of the fused consumer, expected consumer launch on 256 CUs)
     "decode_m1": (1, False, "shard", dict(kind="small_m", ranges=4, tiles=448, grid=448, a_panels=0)),
-    "xover_m128": (128, False, "shard", dict(kind="mfma", tile_config=2, tiles=224, grid=224, split=0,
+    "xover_m128": (128, False, "shard", dict(kind="mfma", tile_config=1, tiles=224, grid=224, split=0,
                                              b_nontemporal=1, tiles_per_wg=1, a_panels=1)),
     "prefill_m4096": (4096, False, "shard", dict(kind="mfma", tile_config=0, tiles=1792, grid=256, split=0,
                                                  b_nontemporal=0, tiles_per_wg=7, a_panels=1)),

@@ -156,7 +156,7 @@ def test_structural_closed_forms(M):
     assert not C3.cpu().numpy().any()
 
 
-@pytest.mark.parametrize("tile_config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile_config", [0, 1, 2])
 @pytest.mark.parametrize("W,M,K,N", [(8, 300, 2048, 1032), (4, 520, 1024, 264)])
 def test_every_tile_config(tile_config, W, M, K, N, monkeypatch):
     """Each MFMA tile configuration (chosen at create time through AGEMM_TILE_CONFIG),

@@ -62,7 +62,7 @@ def test_plan(M, N, split):
 
 
 @pytest.mark.parametrize("mode", ["0", "1"])
-@pytest.mark.parametrize("tile_config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile_config", [0, 1, 2])
 @pytest.mark.parametrize("W,M,K,N", [
     (8, 300, 2048, 1032),   # 10 tiles x 8 shards: many contributors per tile
     (4, 520, 1024, 264),    # 6 tiles x 4 shards, ragged rows and columns

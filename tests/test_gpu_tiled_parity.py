@@ -41,21 +41,21 @@ CASES = {
     # 256x128 tiles, one row block (M just over 128, ragged rows): nontemporal B,
     # 160 workgroups of one tile each
     "t256x128_nontemporal_b": (8, 130, 512, 20480,
-                               dict(kind="mfma", tile_config=4, tiles=160, grid=160, split=0, tiles_per_wg=1,
+                               dict(kind="mfma", tile_config=2, tiles=160, grid=160, split=0, tiles_per_wg=1,
                                     b_nontemporal=1, a_panels=1)),
     # 256x128 tiles, one row block, 300 tiles on 256 workgroups: the cursor crosses
     # tiles, ragged last columns
     "t256x128_persistent": (8, 256, 512, 38392,
-                            dict(kind="mfma", tile_config=4, tiles=300, grid=256, split=0, tiles_per_wg=2,
+                            dict(kind="mfma", tile_config=2, tiles=300, grid=256, split=0, tiles_per_wg=2,
                                  b_nontemporal=1, a_panels=1)),
     # 128x128 tiles, one row block: nontemporal B, 160 workgroups of one tile each
     "t128_nontemporal_b": (8, 96, 1024, 20472,
-                           dict(kind="mfma", tile_config=2, tiles=160, grid=160, split=0, tiles_per_wg=1,
+                           dict(kind="mfma", tile_config=1, tiles=160, grid=160, split=0, tiles_per_wg=1,
                                 b_nontemporal=1, a_panels=1)),
     # 128x128 tiles, one row block, 288 tiles on 256 workgroups: nontemporal B with the
     # cursor crossing tiles
     "t128_nontemporal_b_persistent": (8, 100, 512, 36864,
-                                      dict(kind="mfma", tile_config=2, tiles=288, grid=256, split=0,
+                                      dict(kind="mfma", tile_config=1, tiles=288, grid=256, split=0,
                                            tiles_per_wg=2, b_nontemporal=1, a_panels=1)),
 }
 

@@ -10,42 +10,43 @@ CUS = 256  # MI355X compute units
 
 
 def _tiles(M, N, cfg):
-    bm = 128 if cfg == 2 else 256
-    bn = 128 if cfg in (2, 4) else 256
+    bm = 128 if cfg == 1 else 256
+    bn = 256 if cfg == 0 else 128
     return -(-M // bm) * -(-N // bn)
 
 
 def _default_cfg(M):
-    return 2 if M <= 128 else 4 if M <= 256 else 0
+    return 1 if M <= 128 else 2 if M <= 256 else 0
 
 
 @pytest.mark.parametrize("M,N,cfg,grid,split", [
-    (128, 28672, 2, 224, False),   # crossover workload: 224 whole 128x128 tiles (split loses here)
-    (256, 28672, 4, 224, False),   # one row block of 256x128 tiles
-    (129, 28672, 4, 224, False),
+    (128, 28672, 1, 224, False),   # crossover workload: 224 whole 128x128 tiles (split loses here)
+    (256, 28672, 2, 224, False),   # one row block of 256x128 tiles
+    (129, 28672, 2, 224, False),
     (257, 28672, 0, 224, False),
     (512, 28672, 0, 224, False),   # out-of-order workload: 224 whole 256x256 tiles
     (4096, 28672, 0, 256, False),  # prefill workload: 1792 tiles, 7 per CU
-    (128, 4096, 2, 256, True),     # 32 tiles: split over one workgroup per CU
+    (128, 4096, 1, 256, True),     # 32 tiles: split over one workgroup per CU
     (512, 2048, 0, 128, True),     # 16 tiles x 8 shards = 128 units
-    (9, 256, 2, 16, True),         # 2 tiles x 8 shards
+    (9, 256, 1, 16, True),         # 2 tiles x 8 shards
 ])
 def test_workload_plans(M, N, cfg, grid, split):
     assert agemm.mfma_plan(M, N, 8, CUS) == (cfg, grid, split)
 
 
 def test_forced_modes_and_single_shard():
-    assert agemm.mfma_plan(128, 28672, 8, CUS, split_mode=1) == (2, 256, True)
-    assert agemm.mfma_plan(128, 4096, 8, CUS, split_mode=0) == (2, 32, False)
+    assert agemm.mfma_plan(128, 28672, 8, CUS, split_mode=1) == (1, 256, True)
+    assert agemm.mfma_plan(128, 4096, 8, CUS, split_mode=0) == (1, 32, False)
     for mode in (-1, 0, 1):  # one shard: nothing to split
         assert agemm.mfma_plan(128, 1024, 1, CUS, split_mode=mode)[2] is False
-    assert agemm.mfma_plan(300, 1000, 8, CUS, tile_config=2)[0] == 2
+    assert agemm.mfma_plan(300, 1000, 8, CUS, tile_config=1)[0] == 1
     assert agemm.mfma_plan(100, 1000, 8, CUS, tile_config=0)[0] == 0
+    assert agemm.mfma_plan(100, 1000, 8, CUS, tile_config=2)[0] == 2
 
 
 def test_plan_invariants_over_a_sweep():
     for M, N, W, cus, tc, mode in itertools.product((1, 9, 128, 129, 256, 300, 4096), (8, 264, 4096, 28672),
-                                                    (1, 2, 3, 8, 16), (7, 80, 256, 304), (-1, 0, 2, 4),
+                                                    (1, 2, 3, 8, 16), (7, 80, 256, 304), (-1, 0, 1, 2),
                                                     (-1, 0, 1)):
         cfg, grid, split = agemm.mfma_plan(M, N, W, cus, tc, mode)
         assert cfg == (tc if tc >= 0 else _default_cfg(M))
@@ -60,7 +61,7 @@ def test_plan_invariants_over_a_sweep():
 
 
 @pytest.mark.parametrize("args", [(0, 64, 8, CUS, -1, -1), (8, 4, 8, CUS, -1, -1), (8, 64, 0, CUS, -1, -1),
-                                  (8, 64, 17, CUS, -1, -1), (8, 64, 8, 0, -1, -1), (8, 64, 8, CUS, 5, -1),
+                                  (8, 64, 17, CUS, -1, -1), (8, 64, 8, 0, -1, -1), (8, 64, 8, CUS, 3, -1),
                                   (8, 64, 8, CUS, -1, 2)])
 def test_plan_rejects_bad_arguments(args):
     with pytest.raises(agemm.AgemmError) as ei:
