@@ -324,8 +324,9 @@ def run_sweep(args):
         prewarm(fused_step, args.prewarm_ms)
         n = args.steps
         r = {"M": M, "consumer": ctx.consumer_info()}
-        # fused and the BSP variants interleaved twice, so a clock drift hits them alike
-        for rep in range(2):
+        # fused and the BSP variants interleaved, so a clock drift hits them alike;
+        # each keeps its best of the passes
+        for rep in range(args.sweep_reps):
             r.setdefault("fused_us", []).append(timeit(fused_step, n))
             r.setdefault("bsp_host_sync_us", []).append(timeit(
                 lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], host_sync=True, stream=sc), n))
@@ -388,6 +389,7 @@ def main():
     ap.add_argument("--sweep", default=None,
                     help="comma-separated M values at K=8192, N=28672, W=8: the fused / BSP / Pull ladder "
                          "per M (one JSON object per M, then a markdown table); no headline line")
+    ap.add_argument("--sweep-reps", type=int, default=4, help="interleaved passes per variant in --sweep")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline (the timed sample takes 10 to 20 s)")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps, so the engine clock has settled")
