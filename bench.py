@@ -409,7 +409,7 @@ def main():
         return calibrate_copy(args.steps)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the flag-gated path keeps all W inbox slots in one GPU's HBM "
-              "and this build has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+              "and the library has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.workload in FD_WORKLOADS:
