@@ -341,6 +341,7 @@ def run_sweep(args):
         torch.cuda.synchronize()
         r["consumer_only_us"] = [timeit(lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), n)]
         ctx.check()
+        r["passes"] = {k: [round(float(x), 1) for x in v] for k, v in r.items() if k.endswith("_us")}
         for k in list(r):
             if k.endswith("_us"):
                 r[k] = float(min(r[k]))
