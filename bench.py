@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -81,12 +82,15 @@ def device_peaks(measure: bool) -> dict:
 
 
 def kernel_digest(kind: str) -> str:
-    """Digest of the consumer kernel's sources: counter figures taken from another
-    version of the kernel are not reported."""
+    """Digest of the consumer kernel's sources, comments and blank space left out:
+    counter figures taken from another version of the kernel's code are not reported."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

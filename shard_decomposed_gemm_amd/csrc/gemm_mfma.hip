@@ -16,10 +16,13 @@
 //
 // Data path (BK-wide k-steps, ring of STAGES LDS buffers):
 //   A_s, B -> LDS : 16-byte direct loads (global_load_lds). One uniform base
-//                   pointer per k-step plus a fixed 32-bit offset per lane; A
-//                   rows (BK*2 bytes) and B rows (BN*2 bytes) are stored with
-//                   the 16-byte chunk index XOR-swizzled so that the reads
-//                   below are free of LDS bank conflicts;
+//                   pointer per k-step plus a fixed 32-bit offset per lane. A
+//                   comes from a row-major shard or from the k-panel inbox
+//                   (32-column panels of M rows, where a tile's k-step is one
+//                   contiguous run); A rows (BK*2 bytes) and B rows (BN*2
+//                   bytes) are stored with the 16-byte chunk index
+//                   XOR-swizzled so that the reads below are free of LDS bank
+//                   conflicts;
 //   LDS -> regs   : A fragments with 16-byte reads, B fragments with
 //                   transpose reads (ds_read_b64_tr_b16), which turn the
 //                   N-contiguous B rows into the K-contiguous operand;
@@ -36,13 +39,16 @@
 // cursor step's loads, one every few MFMAs, into the buffer the barrier freed,
 // so they never arrive in a burst that would stall the fragment reads.
 //
-// Tile shapes. Four waves with 128x128 wave tiles (256 fp32 accumulators per
-// lane, held in AGPRs) read a third less LDS per MFMA than eight waves with
-// 128x64 tiles and are the fastest configuration measured on MI355X. At
-// M = 4096 the counters show the MFMA pipes busy about two thirds of the
-// cycles, with the LDS far from saturated and free of bank conflicts: the
-// rest is issue stalls of the one wave per SIMD (fragment-read and
-// direct-load waits, the per-k-step barrier).
+// Tile shapes. Three, all of four waves: 256x256 (128x128 wave tiles, 256
+// fp32 accumulators per lane held in AGPRs: a third less LDS per MFMA than
+// eight waves with 128x64 tiles, which measured slower), 128x128 for M up to
+// 128 and 256x128 for M up to 256 (one row block: B is read once). At
+// M = 4096 the MFMA pipes are busy about 73 % of the cycles at the 1.6-1.7
+// GHz the part holds under this load (a register-only MFMA loop holds 2.4
+// GHz). Copies of the kernel without the barrier or without the waits run no
+// faster; without the A loads it runs 6.5 % faster whatever memory they read:
+// the wave's own issue of loads and fragment reads, and the clock that the
+// power of all of it sets, bound the rate.
 #include "agemm_internal.h"
 #include "mfma_sched.h"
 
