@@ -113,6 +113,8 @@ typedef struct {
  *   AGEMM_SPLIT=0|1          MFMA work split: 0 whole tiles only, 1 the stream-K
  *                            split whenever W >= 2 (default: the split when whole
  *                            tiles would leave at least half of the CUs idle)
+ *   AGEMM_SMALL_M_MAX=0..8   largest M for which the small-M kernel is used
+ *                            (default 1; 0: never)
  *   AGEMM_SMALL_M_PLAN=l,r,w small-M work split: lanes, K-ranges, workgroups per CU
  *   AGEMM_PRODUCER_ITEM_KIB  bytes of one tile copied by one producer workgroup
  *                            (1..1024, default 16) */
@@ -127,8 +129,8 @@ int agemm_tiles(const agemm_ctx* ctx, int64_t* bkf, int32_t* kt, int32_t* t);
 
 /* Consumer kernel the context's GEMM calls launch: *kind = 0 for the MFMA
  * tile kernel (then *tile_config is its tile configuration, 0..2), 1 for the
- * small-M split-K streaming kernel (M <= 8; *tile_config = -1). Either output
- * pointer may be NULL. */
+ * small-M split-K streaming kernel (M = 1 by default, M <= 8 through
+ * AGEMM_SMALL_M_MAX; *tile_config = -1). Either output pointer may be NULL. */
 int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_config);
 
 /* The MFMA consumer's work plan for a shape on a GPU with num_cus compute
@@ -137,7 +139,7 @@ int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_con
  * persistent grid, *split = 1 for the stream-K split. tile_config -1 and
  * split_mode -1 are the automatic choices (AGEMM_TILE_CONFIG / AGEMM_SPLIT
  * give the others). Applies to the MFMA consumer only (a context with
- * M <= 8 uses the small-M kernel). EINVAL for M < 1, N < 8, W outside
+ * M = 1 uses the small-M kernel by default). EINVAL for M < 1, N < 8, W outside
  * 1..16, num_cus < 1 or an out-of-range tile_config / split_mode. Output
  * pointers may be NULL. */
 int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
@@ -210,8 +212,8 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
  * this shape (the MFMA kernel on whole tiles only, never the stream-K split).
  * It allocates nothing: the small-M kernel's split-K workspace is a
  * file-scope device array of the library (8 MiB of fp32 partials, i.e.
- * ranges x M x N <= 2,097,152 with up to 8 K-ranges at M <= 8, and 64 KiB of
- * column counters), held on each device until the process ends. Every call
+ * ranges x M x N <= 2,097,152 with up to 8 K-ranges, the kernel running at
+ * M = 1 here, and 64 KiB of column counters), held on each device until the process ends. Every call
  * on one GPU shares that array: calls that overlap on one GPU (concurrent
  * streams) race and give undefined C; calls in one stream order are fine.
  * Returns AGEMM_ESHAPE for a shape outside the accepted set or whose

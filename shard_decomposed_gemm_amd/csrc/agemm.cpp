@@ -263,7 +263,12 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
   const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 8 * sizeof(uint64_t);  // + probe times
-  c->small_plan = small_m_plan(W, M, KS, N, c->num_cus);
+  int small_max = small_m_default_max();
+  if (const char* env = std::getenv("AGEMM_SMALL_M_MAX")) {
+    const int v = std::atoi(env);
+    if (v >= 0 && v <= small_m_limit()) small_max = v;
+  }
+  if (M <= small_max) c->small_plan = small_m_plan(W, M, KS, N, c->num_cus);
   if (const char* env = std::getenv("AGEMM_SMALL_M_PLAN")) {  // "lanes,ranges,wg_per_cu" override
     int l = 0, r = 0, wpc = 0;
     if (std::sscanf(env, "%d,%d,%d", &l, &r, &wpc) == 3 && c->small_plan.ok) {

@@ -160,7 +160,8 @@ hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s,
 // Overlap probe (probes.hip): times[0..1] = start, end of a kernel that sleeps
 // `ticks` on `first`; times[2] = start of a kernel launched after it on `second`.
 hipError_t launch_overlap_probe(hipStream_t first, hipStream_t second, uint64_t* times, uint64_t ticks);
-int small_m_limit();
+int small_m_limit();         // largest M the small-M kernel takes
+int small_m_default_max();   // largest M for which it is the default consumer
 SmallMPlan small_m_plan(int W, int64_t M, int64_t KS, int64_t N, int num_cus);
 // The plan for given lanes / ranges / workgroups per CU, if the kernel takes it.
 SmallMPlan small_m_plan_with(int W, int64_t M, int64_t KS, int64_t N, int lanes, int ranges, int wg_per_cu);

@@ -332,6 +332,14 @@ hipError_t launch_mt(const SmallMArgs& a, bool out_f32, hipStream_t s, const Lau
 
 int small_m_limit() { return 8; }
 
+// Largest M for which the small-M kernel is the default consumer. From M = 2
+// on, the MFMA kernel on 128x128 tiles (k-panel inbox, nontemporal B) streams
+// B at least as fast. Consumer alone at K = 8192, N = 28672, W = 8, us:
+//   M          1      2      3      4      6      8
+//   small-M   76.5   81.7   96.5  100.1  114.4  121.7
+//   MFMA      78.4   78.8   78.3   78.8   77.9   79.8
+int small_m_default_max() { return 1; }
+
 // Picks (lanes, ranges) for the shape: the highest ratio of useful work to
 // the work of the busiest rounds of workgroup slots (kWgPerCu per CU; 1.0 =
 // every slot streams the same number of B bytes), then the fewest K-ranges

@@ -97,7 +97,7 @@ extern "C" int agemm_pull_noalloc(int W, int64_t M, int64_t K, int64_t N, agemm_
   g.split = 0;             // whole tiles: no workspace
   const bool f32 = c_dtype == AGEMM_F32;
 
-  const SmallMPlan plan = small_m_plan(W, M, KS, N, cus);
+  const SmallMPlan plan = M <= small_m_default_max() ? small_m_plan(W, M, KS, N, cus) : SmallMPlan{};
   hipError_t e;
   if (plan.ok) {
     const size_t ws_bytes = sizeof(float) * (size_t)plan.ranges * (size_t)M * (size_t)N;

@@ -40,3 +40,20 @@ def empty_c(M, N, c_dtype):
 
 def c_to_f64(C) -> np.ndarray:
     return C.float().cpu().numpy().astype(np.float64)
+
+
+def pick_consumer(monkeypatch, kernel):
+    """Selects the consumer of contexts created afterwards: "small_m" lets the small-M
+    streaming kernel take M up to 8 (by default it runs at M = 1 only), "mfma" keeps it
+    off at every M, None leaves the default choice."""
+    if kernel == "small_m":
+        monkeypatch.setenv("AGEMM_SMALL_M_MAX", "8")
+    elif kernel == "mfma":
+        monkeypatch.setenv("AGEMM_SMALL_M_MAX", "0")
+    elif kernel is not None:
+        raise ValueError(kernel)
+
+
+def assert_consumer(ctx, kernel):
+    if kernel is not None:
+        assert ctx.consumer_info()["kind"] == kernel, ctx.consumer_info()

@@ -26,14 +26,20 @@ def gate_mode(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("W,M,K,N", [(8, 1, 2048, 1024), (8, 4, 4096, 2056), (8, 96, 2048, 1024), (8, 512, 2048, 1024)])
-def test_poisoned_inbox_is_never_read_early(W, M, K, N, gate_mode):
+@pytest.mark.parametrize("W,M,K,N,kernel", [
+    (8, 1, 2048, 1024, "small_m"), (8, 1, 2048, 1024, "mfma"),
+    (8, 4, 4096, 2056, "small_m"), (8, 4, 4096, 2056, "mfma"),
+    (8, 96, 2048, 1024, "mfma"), (8, 512, 2048, 1024, "mfma"),
+])
+def test_poisoned_inbox_is_never_read_early(W, M, K, N, kernel, gate_mode, monkeypatch):
     """Epochs 1 and 2 fill both inboxes with NaN; epoch 3 releases real tiles late and
     out of order while the consumer is already running. Any premature read would show NaN."""
     import torch
     a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=41)
     ref = oracle.sharded_gemm(sh, b)
+    gu.pick_consumer(monkeypatch, kernel)
     ctx = _ctx(W, M, K, N, "f32")
+    gu.assert_consumer(ctx, kernel)
     nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
     ctx.produce(nan)
     ctx.produce(nan)  # epochs alternate between two inboxes: poison both
@@ -50,14 +56,15 @@ def test_poisoned_inbox_is_never_read_early(W, M, K, N, gate_mode):
     assert np.abs(got - ref).max() <= oracle.tolerance(K)
 
 
-@pytest.mark.parametrize("W,M,K,N,bkf", [
-    (8, 300, 8192, 1000, 128),   # 256x256 MFMA tiles, 8 flag tiles per shard
-    (8, 130, 4096, 520, 64),     # 128x128 MFMA tiles, one k-step per flag tile
-    (8, 4, 4096, 1032, 64),      # small-M streaming kernel
-    (8, 1, 4096, 1024, 64),      # small-M, M = 1
-    (16, 257, 16384, 264, 256),  # 16 shards of 4 flag tiles
+@pytest.mark.parametrize("W,M,K,N,bkf,kernel", [
+    (8, 300, 8192, 1000, 128, None),   # 256x256 MFMA tiles, 8 flag tiles per shard
+    (8, 130, 4096, 520, 64, None),     # 128x128 MFMA tiles, one k-step per flag tile
+    (8, 4, 4096, 1032, 64, "small_m"), # small-M streaming kernel
+    (8, 4, 4096, 1032, 64, "mfma"),    # the same on 128x128 MFMA tiles (the default at M = 4)
+    (8, 1, 4096, 1024, 64, "small_m"), # small-M, M = 1
+    (16, 257, 16384, 264, 256, None),  # 16 shards of 4 flag tiles
 ])
-def test_sixty_four_flags_out_of_order(W, M, K, N, bkf):
+def test_sixty_four_flags_out_of_order(W, M, K, N, bkf, kernel, monkeypatch):
     """The largest flag count, T = W * KS / BK_f = 64 (one flag per lane of the polling
     wave), with a non-default flag k-tile: poisoned inboxes, then the 64 tiles released
     in a seeded order with cumulative delays while the consumer runs."""
@@ -65,7 +72,9 @@ def test_sixty_four_flags_out_of_order(W, M, K, N, bkf):
     from shard_decomposed_gemm_amd import Context
     a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=43)
     ref = oracle.sharded_gemm(sh, b)
+    gu.pick_consumer(monkeypatch, kernel)
     ctx = Context(W, M, K, N, c_dtype="f32", flag_ktile=bkf)
+    gu.assert_consumer(ctx, kernel)
     assert ctx.t == 64
     nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
     ctx.produce(nan)
@@ -108,7 +117,7 @@ def test_alternating_epochs(M, gate_mode):
         assert np.abs(gu.c_to_f64(C) - refs[e % 3]).max() <= oracle.tolerance(K), e
 
 
-@pytest.mark.parametrize("M", [2, 300])
+@pytest.mark.parametrize("M", [1, 2, 300])
 def test_timeout_reports_and_recovers(M):
     """A tile released long after the consumer's spin timeout: the consumer stops,
     agemm_check reports ETIMEOUT, and the next epoch is correct again."""
@@ -208,8 +217,9 @@ def test_flag_tiles_above_31_wait_when_tile_31_is_up(split, monkeypatch):
     ctx.close()
 
 
-@pytest.mark.parametrize("M,epochs", [(1, 120), (7, 120), (300, 120), (1024, 120), (512, 1000)])
-def test_epoch_stress_bitwise(M, epochs, gate_mode):
+@pytest.mark.parametrize("M,epochs,kernel", [(1, 120, None), (7, 120, "small_m"), (7, 120, "mfma"), (300, 120, None),
+                                            (1024, 120, None), (512, 1000, None)])
+def test_epoch_stress_bitwise(M, epochs, kernel, gate_mode, monkeypatch):
     """120 (at M = 512: 1000) epochs cycle three data sets with jittered release schedules while the
     consumer runs concurrently. Each epoch's C must equal, bit for bit, the ungated
     (pull) result of its own data set: a read of an inbox's previous content (another
@@ -217,7 +227,9 @@ def test_epoch_stress_bitwise(M, epochs, gate_mode):
     import torch
     W, K, N = 8, 2048, 1544
     probs = [gu.random_problem(W, M, K, N, seed=s) for s in (81, 82, 83)]
+    gu.pick_consumer(monkeypatch, kernel)
     ctx = _ctx(W, M, K, N, "f16")
+    gu.assert_consumer(ctx, kernel)
     refs = []
     for p in probs:
         C = gu.empty_c(M, N, "f16")

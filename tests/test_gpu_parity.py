@@ -70,11 +70,11 @@ def test_tiny_config_against_stored_golden(path, c_dtype):
 
 
 SHAPES = [
-    # W, M, K, N                      kernel exercised
-    (8, 8, 512, 256),                 # small-M, tiny workload
+    # W, M, K, N                      kernel exercised (default choice)
+    (8, 8, 512, 256),                 # 128x128 MFMA tiles, stream-K split, tiny workload
     (8, 1, 2048, 1000),               # small-M, ragged column block
-    (4, 3, 1024, 4104),               # small-M, M not a power of two
-    (2, 7, 256, 72),                  # small-M, W = 2
+    (4, 3, 1024, 4104),               # 128x128 MFMA tiles, M not a power of two
+    (2, 7, 256, 72),                  # 128x128 MFMA tile, W = 2, one ragged tile
     (8, 130, 2048, 520),              # 128x128 MFMA tiles, ragged rows and columns
     (1, 40, 512, 136),                # W = 1 (no decomposition)
     (8, 300, 2048, 1000),             # 256x256 MFMA tiles, ragged rows and columns
@@ -117,6 +117,60 @@ def test_parity_exact_inputs(W, M, K, N, path):
             assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
         else:
             assert np.array_equal(C.cpu().numpy().view(np.uint16), ref.astype(np.float16).view(np.uint16))
+
+
+# The small-M streaming kernel takes M up to 8 when asked (AGEMM_SMALL_M_MAX); by
+# default it runs at M = 1 only.
+SMALL_M_SHAPES = [
+    (8, 8, 512, 256),                 # tiny workload
+    (8, 2, 2048, 1000),               # ragged column block
+    (4, 3, 1024, 4104),               # M not a power of two
+    (2, 7, 256, 72),                  # W = 2
+    (16, 5, 2048, 264),               # 16 shards
+]
+
+
+@pytest.mark.parametrize("W,M,K,N", SMALL_M_SHAPES)
+@pytest.mark.parametrize("path", ["fused", "bsp", "pull"])
+def test_small_m_kernel_up_to_m8(W, M, K, N, path, monkeypatch):
+    """The small-M kernel at 1 < M <= 8: uniform inputs within the tolerance (fp16 and
+    fp32 C), and exact inputs bit for bit."""
+    gu.pick_consumer(monkeypatch, "small_m")
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=W * 11 + M)
+    ref = oracle.sharded_gemm(sh, b)
+    for c_dtype in ("f16", "f32"):
+        ctx = _ctx(W, M, K, N, c_dtype)
+        gu.assert_consumer(ctx, "small_m")
+        C = gu.empty_c(M, N, c_dtype)
+        _run(ctx, path, dsh, B, C)
+        assert np.abs(gu.c_to_f64(C) - ref).max() <= oracle.tolerance(K), c_dtype
+    a = gu.coarse_bits(0xC200 + M, M, K)
+    b = gu.coarse_bits(0xC300 + N, K, N)
+    sh = synth.shards(a, W)
+    ref = oracle.sharded_gemm(sh, b)
+    ctx = _ctx(W, M, K, N, "f32")
+    C = gu.empty_c(M, N, "f32")
+    _run(ctx, path, [gu.to_dev(s) for s in sh], gu.to_dev(b), C)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
+
+
+def test_default_consumer_by_m(monkeypatch):
+    """The small-M kernel is the default at M = 1 only; AGEMM_SMALL_M_MAX moves the cutoff
+    (0: never, up to 8)."""
+    W, K, N = 8, 1024, 1024
+    for M, kind in ((1, "small_m"), (2, "mfma"), (8, "mfma"), (9, "mfma")):
+        ctx = _ctx(W, M, K, N, "f16")
+        assert ctx.consumer_info()["kind"] == kind, (M, ctx.consumer_info())
+        ctx.close()
+    monkeypatch.setenv("AGEMM_SMALL_M_MAX", "0")
+    ctx = _ctx(W, 1, K, N, "f16")
+    assert ctx.consumer_info()["kind"] == "mfma"
+    ctx.close()
+    monkeypatch.setenv("AGEMM_SMALL_M_MAX", "8")
+    for M, kind in ((8, "small_m"), (9, "mfma")):
+        ctx = _ctx(W, M, K, N, "f16")
+        assert ctx.consumer_info()["kind"] == kind, (M, ctx.consumer_info())
+        ctx.close()
 
 
 @pytest.mark.parametrize("M", [1, 8, 200, 512])

@@ -1,8 +1,9 @@
 """Seeded random shapes through every path, bit for bit against the oracle.
 
 Shapes drawn from a fixed seed: W from 1 to 16 shards (odd counts included),
-shard widths KS from 64 to 512 columns, M from 1 to 600 rows (the small-M
-streaming kernel and every MFMA tile), N from 8 to 1600 columns in steps of 8
+shard widths KS from 64 to 512 columns, M from 1 to 600 rows (every MFMA
+tile, and the small-M streaming kernel: by default at M = 1, and on the
+shapes with 1 < M <= 8 once more with it asked for), N from 8 to 1600 columns in steps of 8
 (ragged tiles), and a flag k-tile chosen among those that divide KS. Inputs
 on a 1/16 grid make every fp32 partial sum exact, so the fused path (tiles
 released in a seeded random order with delays, into inboxes full of NaN), the
@@ -37,13 +38,15 @@ def _shapes(n=40, seed=0x5EED):
 
 
 SHAPES = _shapes()
+CASES = [s + (None,) for s in SHAPES] + [s + ("small_m",) for s in SHAPES if 1 < s[1] <= 8]
 
 
-@pytest.mark.parametrize("W,M,K,N,bkf", SHAPES)
-def test_random_shape_every_path_exact(W, M, K, N, bkf):
+@pytest.mark.parametrize("W,M,K,N,bkf,kernel", CASES)
+def test_random_shape_every_path_exact(W, M, K, N, bkf, kernel, monkeypatch):
     import torch
     from shard_decomposed_gemm_amd import Context
-    print(f"[random-shape] W={W} M={M} K={K} N={N} flag_ktile={bkf}", flush=True)
+    print(f"[random-shape] W={W} M={M} K={K} N={N} flag_ktile={bkf} consumer={kernel or 'default'}", flush=True)
+    gu.pick_consumer(monkeypatch, kernel)
     a = gu.coarse_bits(0x9000 + M + N, M, K)
     b = gu.coarse_bits(0x9100 + K, K, N)
     sh = synth.shards(a, W)
@@ -51,6 +54,7 @@ def test_random_shape_every_path_exact(W, M, K, N, bkf):
     dsh = [gu.to_dev(s) for s in sh]
     B = gu.to_dev(b)
     ctx = Context(W, M, K, N, c_dtype="f32", flag_ktile=bkf)
+    gu.assert_consumer(ctx, kernel)
     sp, sc = ctx.streams()
     nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
     ctx.produce(nan, stream=sp)
