@@ -1,4 +1,5 @@
-// Flag-gated shard-decomposed GEMM for few rows (M <= 8): streaming B.
+// Flag-gated shard-decomposed GEMM for few rows (M <= 8; the default
+// consumer at M = 1, see small_m_default_max below): streaming B.
 //
 // With one (or a handful of) rows of A, C = sum_s A_s . B[s*KS:(s+1)*KS, :]
 // ("Eliminating Multi-GPU Performance Taxes" analysis page, AG+GEMM core
