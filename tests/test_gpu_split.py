@@ -71,21 +71,29 @@ def test_plan(M, N, split):
 ])
 def test_split_exact_bitwise(W, M, K, N, tile_config, mode, monkeypatch):
     """Exact inputs (every product and partial sum exact in fp32): split and whole-tile
-    results must both equal the oracle bit for bit, on every path, with the producer
-    releasing tiles out of order while the fused consumer runs."""
+    results must both equal the oracle bit for bit (fp32 C) or its round-to-nearest-even
+    (fp16 C), on every path, with the producer releasing tiles out of order while the
+    fused consumer runs."""
     monkeypatch.setenv("AGEMM_TILE_CONFIG", str(tile_config))
     monkeypatch.setenv("AGEMM_SPLIT", mode)
     a = gu.coarse_bits(0xF000 + M, M, K)
     b = gu.coarse_bits(0xF100 + N, K, N)
     sh = synth.shards(a, W)
     ref = oracle.sharded_gemm(sh, b)
-    ctx = _ctx(W, M, K, N, "f32")
-    assert ctx.split is (mode == "1")
-    sched = synth.schedule(0xF200 + tile_config, ctx.t, 8_000)
-    outs = _paths(ctx, [gu.to_dev(s) for s in sh], gu.to_dev(b), "f32", sched)
-    for path, C in outs.items():
-        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), (path, tile_config, mode)
-    ctx.close()
+    dsh = [gu.to_dev(s) for s in sh]
+    B = gu.to_dev(b)
+    for c_dtype in ("f32", "f16"):
+        ctx = _ctx(W, M, K, N, c_dtype)
+        assert ctx.split is (mode == "1")
+        sched = synth.schedule(0xF200 + tile_config, ctx.t, 8_000)
+        outs = _paths(ctx, dsh, B, c_dtype, sched)
+        for path, C in outs.items():
+            if c_dtype == "f32":
+                assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), (path, tile_config, mode)
+            else:
+                assert np.array_equal(C.cpu().numpy().view(np.uint16), ref.astype(np.float16).view(np.uint16)), \
+                    (path, tile_config, mode)
+        ctx.close()
 
 
 @pytest.mark.parametrize("c_dtype", ["f16", "f32"])
