@@ -409,9 +409,17 @@ def main():
                          "for counter collection, which serialises kernel dispatches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--probe-mfma", type=int, default=0, metavar="LAUNCHES",
+                    help="only run the register-only fp16 MFMA loop for LAUNCHES launches (about 1.8 ms each) "
+                         "and print its rate: a pure MFMA load, e.g. to read clocks and power beside the GEMM's")
     args = ap.parse_args()
     if args.calibrate_copy:
         return calibrate_copy(args.steps)
+    if args.probe_mfma > 0:
+        from shard_decomposed_gemm_amd import agemm
+        print(json.dumps({"probe": "fp16 MFMA register loop", "launches": args.probe_mfma,
+                          "tflops": agemm.probe_mfma(10, args.probe_mfma)}), flush=True)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the flag-gated path keeps all W inbox slots in one GPU's HBM "
               "and the library has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
