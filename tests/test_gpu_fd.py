@@ -50,6 +50,7 @@ SHAPES = [
     (1, 32, 64, 8),     # one rank: the combine is the identity
     (16, 64, 256, 16),  # 16 ranks, d = 256
     (3, 20, 128, 4),    # odd rank count, heads not a multiple of 4 waves
+    (2, 1024, 64, 32),  # the largest head tile (32 heads per flag), 1024 heads, T = 64
 ]
 
 
