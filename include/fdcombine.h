@@ -38,7 +38,8 @@
  * call launches nothing and changes no state), and is asynchronous on the
  * given stream (a hipStream_t passed as void*; NULL = the null stream).
  * Device-side flag waits time out after the spin timeout; fdc_check then
- * reports AGEMM_ETIMEOUT and that call's O is undefined.
+ * reports AGEMM_ETIMEOUT and that call's O is undefined. A context is not
+ * thread-safe; use one per host thread.
  */
 #ifndef FDCOMBINE_H_
 #define FDCOMBINE_H_
