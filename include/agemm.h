@@ -117,7 +117,12 @@ typedef struct {
  *                            (default 1; 0: never)
  *   AGEMM_SMALL_M_PLAN=l,r,w small-M work split: lanes, K-ranges, workgroups per CU
  *   AGEMM_PRODUCER_ITEM_KIB  bytes of one tile copied by one producer workgroup
- *                            (1..1024, default 16) */
+ *                            (1..1024, default 16)
+ *   AGEMM_EPOCH_BASE=n       testing: both inboxes' epoch counts start at n (flags
+ *                            set to match), so that a few calls take the 32-bit
+ *                            flag counters across their wrap (n = 2^32 - 3 wraps
+ *                            on the third call per inbox); anything but a number
+ *                            in 0..2^32-1 makes agemm_create return EINVAL */
 int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype,
                  int64_t flag_ktile);
 

@@ -56,7 +56,11 @@ typedef struct fdc_ctx fdc_ctx;
 
 /* Creates a context for one shape on the current device: two inboxes (used by
  * alternate epochs) of W x T/W blocks, their flags (zeroed), the gather
- * buffer of the baseline and the error word. out_dtype: output dtype. */
+ * buffer of the baseline and the error word. out_dtype: output dtype.
+ * AGEMM_EPOCH_BASE=n in the environment (testing) starts both inboxes' epoch
+ * and consumed counts at n, with the flags to match, so that a few calls take
+ * the 32-bit counters across their wrap (anything but a number in 0..2^32-1:
+ * EINVAL). */
 int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dtype out_dtype);
 
 /* Frees everything the context owns after synchronising the device. NULL is accepted. */

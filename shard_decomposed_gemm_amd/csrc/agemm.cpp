@@ -190,6 +190,9 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   if (!out) return AGEMM_EINVAL;
   *out = nullptr;
   if (c_dtype != AGEMM_F16 && c_dtype != AGEMM_F32) return AGEMM_EINVAL;
+  uint32_t base = 0;
+  const int has_base = epoch_base_from_env(&base);
+  if (has_base < 0) return AGEMM_EINVAL;
   if (W < 1 || W > kMaxShards || M < 1 || M > INT32_MAX || K < 1 || N < 8) return AGEMM_ESHAPE;
   if (K % W) return AGEMM_ESHAPE;
   const int64_t KS = K / W;
@@ -318,6 +321,12 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     void* dp = nullptr;
     e = hipHostGetDevicePointer(&dp, hp, 0);
     c->err_dev = static_cast<ErrWord*>(dp);
+  }
+  if (e == hipSuccess && has_base > 0) {
+    // every produce on an inbox adds items_per_tile to each of its flags
+    c->slot_epochs[0] = c->slot_epochs[1] = base;
+    const std::vector<uint32_t> init(2 * kMaxTiles, base * (uint32_t)c->items_per_tile);
+    e = hipMemcpy(c->ctrl, init.data(), init.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = c->so.create();
   if (e == hipSuccess) e = hipDeviceSynchronize();

@@ -125,6 +125,9 @@ int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dty
   if (!out) return AGEMM_EINVAL;
   *out = nullptr;
   if (out_dtype != AGEMM_F16 && out_dtype != AGEMM_F32) return AGEMM_EINVAL;
+  uint32_t base = 0;
+  const int has_base = epoch_base_from_env(&base);
+  if (has_base < 0) return AGEMM_EINVAL;
   const int HT = heads_per_tile;
   if (W < 1 || W > kMaxShards || H < 1 || (D != 64 && D != 128 && D != 256)) return AGEMM_ESHAPE;
   if (HT < 4 || HT > 32 || HT % 4 || H % HT) return AGEMM_ESHAPE;
@@ -180,6 +183,16 @@ int fdc_create(fdc_ctx** out, int W, int H, int D, int heads_per_tile, agemm_dty
     void* dp = nullptr;
     e = hipHostGetDevicePointer(&dp, hp, 0);
     c->err_dev = static_cast<ErrWord*>(dp);
+  }
+  if (e == hipSuccess && has_base > 0) {
+    // every produce on an inbox adds one to each of its flags; every fused
+    // combine on it adds H to its consumed count
+    c->slot_epochs[0] = c->slot_epochs[1] = base;
+    c->fused_issued[0] = c->fused_issued[1] = base;
+    const std::vector<uint32_t> init(2 * kMaxTiles, base);
+    e = hipMemcpy(c->ctrl, init.data(), init.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+    const uint32_t counts[2] = {base * (uint32_t)c->L.H, base * (uint32_t)c->L.H};
+    if (e == hipSuccess) e = hipMemcpy(c->consumed[0], counts, sizeof counts, hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = c->so.create();
   if (e == hipSuccess) e = hipDeviceSynchronize();

@@ -1,8 +1,10 @@
 // Host-side pieces shared by the GEMM and Flash-Decode combine contexts.
 #include "host_common.h"
 
+#include <cerrno>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 
 namespace agemm {
 
@@ -10,6 +12,17 @@ namespace {
 const char* kStatusNames[] = {"AGEMM_OK",  "AGEMM_EINVAL",   "AGEMM_ESHAPE", "AGEMM_ENOMEM",
                               "AGEMM_EHIP", "AGEMM_ETIMEOUT", "AGEMM_ESTATE"};
 }  // namespace
+
+int epoch_base_from_env(uint32_t* base) {
+  const char* env = std::getenv("AGEMM_EPOCH_BASE");
+  if (!env) return 0;
+  char* end = nullptr;
+  errno = 0;
+  const unsigned long long v = std::strtoull(env, &end, 0);
+  if (!*env || *end || errno || v > 0xffffffffull || env[0] == '-') return -1;
+  *base = (uint32_t)v;
+  return 1;
+}
 
 const char* status_name(int code) {
   if (code < 0 || code > AGEMM_ESTATE) return "AGEMM_UNKNOWN";

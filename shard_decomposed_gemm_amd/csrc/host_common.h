@@ -22,6 +22,13 @@ const char* status_name(int code);
 
 inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Testing hook: when AGEMM_EPOCH_BASE is set, a new context starts both
+// inboxes' epoch counts at its value (and sets its flags and counts to
+// match), so that a few calls take the 32-bit counters across their wrap.
+// Returns 1 and sets *base when it is set to a number in 0..2^32-1, 0 when it
+// is unset, -1 when it holds anything else (the context is then refused).
+int epoch_base_from_env(uint32_t* base);
+
 // Validates a release schedule for T tiles and converts it for the producer:
 // order[p] = tile released p-th, offset_ticks[p] = its release time in
 // wall-clock ticks, *has_delay = any offset non-zero. sched == NULL is tile

@@ -166,6 +166,54 @@ def test_fd_alternating_epochs():
         assert np.abs(O.cpu().numpy().astype(np.float64) - refs[e % 3]).max() <= fdo.tolerance("f32"), e
 
 
+def test_fd_epochs_across_the_counter_wrap(monkeypatch):
+    """AGEMM_EPOCH_BASE = 2^32 - 3 starts the flags' and consumed counts' epochs just below
+    their 32-bit wrap (both are compared by wrap-aware differences). After two epochs of
+    NaN partials, eight epochs with three data sets, tiles released late and out of
+    order, take every count across the wrap. Each output must match its own partials: the
+    rank-order BSP result of a context counting from zero, within the tolerance (the
+    fused combine folds ranks in arrival order)."""
+    import torch
+    W, H, D, HT = 8, 96, 128, 16
+    sets = [synth.fd_partials(0x7800 + 16 * k, W, H, D) for k in range(3)]
+    devs = [_dev_parts(o, l) for o, l in sets]
+    plain = _ctx(W, H, D, HT, "f32")
+    refs = []
+    for k in range(3):
+        O = _out(H, D, "f32")
+        plain.run_bsp(*devs[k], O)
+        refs.append(O)
+    torch.cuda.synchronize()
+    plain.check()
+    assert np.abs(refs[0].cpu().numpy().astype(np.float64) - fdo.combine(*sets[0])).max() <= fdo.tolerance("f32")
+    from shard_decomposed_gemm_amd import AgemmError
+    from shard_decomposed_gemm_amd.agemm import EINVAL
+    monkeypatch.setenv("AGEMM_EPOCH_BASE", "0x1ffffffff")  # past 32 bits: refused, so the hook is read
+    with pytest.raises(AgemmError) as ei:
+        _ctx(W, H, D, HT, "f32")
+    assert ei.value.status == EINVAL
+    monkeypatch.setenv("AGEMM_EPOCH_BASE", str(2**32 - 3))
+    ctx = _ctx(W, H, D, HT, "f32")
+    sp, sc = ctx.streams()
+    nan_o = [torch.full((H, D), float("nan"), dtype=torch.float32, device=gu.dev()) for _ in range(W)]
+    nan_l = [torch.full((H,), float("nan"), dtype=torch.float32, device=gu.dev()) for _ in range(W)]
+    ctx.produce(nan_o, nan_l, stream=sp)
+    ctx.produce(nan_o, nan_l, stream=sp)
+    outs = []
+    for e in range(8):
+        k = e % 3
+        order, offs = synth.schedule(0x7900 + e, ctx.t, 3_000)
+        O = _out(H, D, "f32")
+        ctx.produce(*devs[k], schedule=(order, offs), stream=sp)
+        ctx.run_fused(O, stream=sc)
+        outs.append(O)
+    torch.cuda.synchronize()
+    ctx.check()
+    for e, O in enumerate(outs):
+        assert np.abs(O.cpu().numpy().astype(np.float64) - refs[e % 3].cpu().numpy().astype(np.float64)).max() \
+            <= fdo.tolerance("f32"), e
+
+
 def test_fd_inbox_guard_holds_the_producer_for_a_late_combine():
     """The combine of epoch 0 starts late (its stream first runs a long matrix product),
     after the producers of epochs 1 and 2 were issued. Epoch 2 reuses epoch 0's inbox:

@@ -117,6 +117,52 @@ def test_alternating_epochs(M, gate_mode):
         assert np.abs(gu.c_to_f64(C) - refs[e % 3]).max() <= oracle.tolerance(K), e
 
 
+@pytest.mark.parametrize("M", [1, 130, 512])
+def test_epochs_across_the_flag_counter_wrap(M, monkeypatch):
+    """The flags are 32-bit counters, compared with each epoch's target by a wrap-aware
+    difference. AGEMM_EPOCH_BASE = 2^32 - 3 starts both inboxes' epoch counts just below
+    the wrap, so that the calls after two poisoning ones take every flag and target
+    across it. Each epoch's C (three data sets cycling, tiles released late and out of
+    order into inboxes that held NaN or another data set) must equal its own Pull result
+    bit for bit."""
+    import torch
+    from shard_decomposed_gemm_amd import AgemmError
+    from shard_decomposed_gemm_amd.agemm import EINVAL
+    W, K, N = 8, 2048, 1544
+    for bad in ("4294967296", "-1", "base"):  # the hook is read: values it cannot take are refused
+        monkeypatch.setenv("AGEMM_EPOCH_BASE", bad)
+        with pytest.raises(AgemmError) as ei:
+            _ctx(W, M, K, N, "f16")
+        assert ei.value.status == EINVAL, bad
+    monkeypatch.setenv("AGEMM_EPOCH_BASE", str(2**32 - 3))
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (91, 92, 93)]
+    ctx = _ctx(W, M, K, N, "f16")
+    refs = []
+    for p in probs:
+        C = gu.empty_c(M, N, "f16")
+        ctx.run_pull(p[3], p[4], C)
+        refs.append(C)
+    torch.cuda.synchronize()
+    assert np.abs(gu.c_to_f64(refs[0]) - oracle.sharded_gemm(probs[0][1], probs[0][2])).max() <= oracle.tolerance(K)
+    sp, sc = ctx.streams()
+    nan = [torch.full((M, K // W), float("nan"), dtype=torch.float16, device=gu.dev()) for _ in range(W)]
+    ctx.produce(nan, stream=sp)
+    ctx.produce(nan, stream=sp)
+    outs = []
+    for e in range(8):  # epoch counts 2^32 - 1, 0, 1, 2 on each inbox
+        p = probs[e % 3]
+        order, offs = synth.schedule(0x5400 + e, ctx.t, 10_000)
+        C = gu.empty_c(M, N, "f16")
+        ctx.produce(p[3], schedule=(order, offs), stream=sp)
+        ctx.run_fused(p[4], C, stream=sc)
+        outs.append(C)
+    torch.cuda.synchronize()
+    ctx.check()
+    for e, C in enumerate(outs):
+        assert torch.equal(C.view(torch.int16), refs[e % 3].view(torch.int16)), e
+    ctx.close()
+
+
 @pytest.mark.parametrize("M", [1, 2, 300])
 def test_timeout_reports_and_recovers(M):
     """A tile released long after the consumer's spin timeout: the consumer stops,
