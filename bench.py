@@ -194,6 +194,24 @@ def fd_cpu_baseline(W, H, D, budget_s: float):
             "sample": f"{n} combines of W={W} partials (H={H}, D={D}, binary64) in {dt:.2f} s", "seconds": dt}
 
 
+def interleaved_ladder(variants, n: int, reps: int, timeit):
+    """Times each variant (name, step function, enter, leave; enter and leave may be None)
+    in `reps` interleaved passes of n steps, the order rotated by one every pass, so that a
+    drift of the clock hits every variant alike. Returns the best pass of each variant and
+    every pass's value (microseconds per step)."""
+    passes = {v[0]: [] for v in variants}
+    for rep in range(reps):
+        k = rep % len(variants)
+        for name, fn, enter, leave in variants[k:] + variants[:k]:
+            if enter:
+                enter()
+            passes[name].append(timeit(fn, n))
+            if leave:
+                leave()
+    return ({name: float(min(v)) for name, v in passes.items()},
+            {name: [round(float(x), 1) for x in v] for name, v in passes.items()})
+
+
 def run_fd(args):
     """One step = producer of the W ranks' partial tiles (seeded release order and
     delays) || flag-gated combine, on two streams."""
@@ -257,16 +275,25 @@ def run_fd(args):
             "note": "latency-bound: 0.4 MB per launch is far below what one launch takes to stream at HBM speed"}
     ladder = None
     if not args.no_ladder:
-        n = args.steps
-        bsp_sync = timeit(lambda i: ctx.run_bsp(do, dl, Os[i & 1], schedule=sched, host_sync=True, stream=sc), n)
-        bsp_dev = timeit(lambda i: ctx.run_bsp(do, dl, Os[i & 1], schedule=sched, host_sync=False, stream=sc), n)
-        fused = timeit(step, n)
-        ctx.produce(do, dl)
-        torch.cuda.synchronize()
-        alone = timeit(lambda i: ctx.run_fused(Os[i & 1], stream=sc), n)
+        def flags_up():
+            ctx.produce(do, dl)
+            torch.cuda.synchronize()
+
+        best, passes = interleaved_ladder([
+            ("bsp_host_sync_us", lambda i: ctx.run_bsp(do, dl, Os[i & 1], schedule=sched, host_sync=True, stream=sc),
+             None, None),
+            ("bsp_device_dep_us", lambda i: ctx.run_bsp(do, dl, Os[i & 1], schedule=sched, host_sync=False, stream=sc),
+             None, None),
+            ("fused_us", step, None, None),
+            ("consumer_only_us", lambda i: ctx.run_fused(Os[i & 1], stream=sc), flags_up, None),
+        ], max(20, args.steps // args.sweep_reps), args.sweep_reps, timeit)
         ctx.check()
-        ladder = {"bsp_host_sync_us": bsp_sync, "bsp_device_dep_us": bsp_dev, "fused_us": fused,
-                  "consumer_only_us": alone, "fused_speedup_vs_bsp": bsp_sync / fused}
+        ladder = dict(best)
+        ladder["fused_speedup_vs_bsp"] = best["bsp_host_sync_us"] / best["fused_us"]
+        ladder["fused_speedup_vs_bsp_device_dep"] = best["bsp_device_dep_us"] / best["fused_us"]
+        ladder["method"] = (f"best of {args.sweep_reps} interleaved passes of "
+                            f"{max(20, args.steps // args.sweep_reps)} steps, order rotated each pass")
+        ladder["passes"] = passes
         print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
     peaks = device_peaks(not args.no_peaks)
     if "measured" in peaks:
@@ -394,7 +421,8 @@ def main():
     ap.add_argument("--sweep", default=None,
                     help="comma-separated M values at K=8192, N=28672, W=8: the fused / BSP / Pull ladder "
                          "per M (one JSON object per M, then a markdown table); no headline line")
-    ap.add_argument("--sweep-reps", type=int, default=4, help="interleaved passes per variant in --sweep")
+    ap.add_argument("--sweep-reps", type=int, default=4,
+                    help="interleaved passes per variant in the ladder and in --sweep (the best pass is kept)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline (the timed sample takes 10 to 20 s)")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warmup steps, so the engine clock has settled")
@@ -529,23 +557,28 @@ def main():
             torch.cuda.synchronize()
             return (time.perf_counter() - t) * 1e6 / n
 
-        n = args.steps
-        bsp_sync = timeit(lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched, host_sync=True,
-                                                stream=sc), n)
-        bsp_dev = timeit(lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched, host_sync=False,
-                                               stream=sc), n)
-        fused = timeit(fused_step, n)
-        ctx.set_strict_acquire(True)
-        fused_strict = timeit(fused_step, n)
-        ctx.set_strict_acquire(False)
-        ctx.produce(shards)
-        torch.cuda.synchronize()
-        consumer_only = timeit(lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), n)
-        pull = timeit(lambda i: ctx.run_pull(shards, Bs[i & 1], Cs[i & 1], stream=sc), n)
+        def flags_up():
+            ctx.produce(shards)
+            torch.cuda.synchronize()
+
+        n = max(20, args.steps // args.sweep_reps)
+        best, passes = interleaved_ladder([
+            ("bsp_host_sync_us", lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched, host_sync=True,
+                                                       stream=sc), None, None),
+            ("bsp_device_dep_us", lambda i: ctx.run_bsp(shards, Bs[i & 1], Cs[i & 1], schedule=sched,
+                                                        host_sync=False, stream=sc), None, None),
+            ("fused_us", fused_step, None, None),
+            ("fused_strict_acquire_us", fused_step, lambda: ctx.set_strict_acquire(True),
+             lambda: ctx.set_strict_acquire(False)),
+            ("consumer_only_us", lambda i: ctx.run_fused(Bs[i & 1], Cs[i & 1], stream=sc), flags_up, None),
+            ("pull_us", lambda i: ctx.run_pull(shards, Bs[i & 1], Cs[i & 1], stream=sc), None, None),
+        ], n, args.sweep_reps, timeit)
         ctx.check()
-        ladder = {"bsp_host_sync_us": bsp_sync, "bsp_device_dep_us": bsp_dev, "fused_us": fused,
-                  "fused_strict_acquire_us": fused_strict, "consumer_only_us": consumer_only, "pull_us": pull,
-                  "fused_speedup_vs_bsp": bsp_sync / fused, "fused_speedup_vs_bsp_device_dep": bsp_dev / fused}
+        ladder = dict(best)
+        ladder["fused_speedup_vs_bsp"] = best["bsp_host_sync_us"] / best["fused_us"]
+        ladder["fused_speedup_vs_bsp_device_dep"] = best["bsp_device_dep_us"] / best["fused_us"]
+        ladder["method"] = f"best of {args.sweep_reps} interleaved passes of {n} steps, order rotated each pass"
+        ladder["passes"] = passes
         print(f"[bench] ladder: {json.dumps(ladder)}", file=sys.stderr, flush=True)
 
     peaks = device_peaks(not args.no_peaks)
