@@ -95,6 +95,23 @@ def test_create_rejects_bad_flag_tile_and_dtype():
     assert lib.agemm_create(None, 8, 4, 8192, 256, agemm.F16, 0) == agemm.EINVAL
 
 
+@pytest.mark.parametrize("value", ["4294967296", "-1", "0x1ffffffff", "12abc", ""])
+def test_epoch_base_hook_refuses_values_it_cannot_take(value, monkeypatch):
+    """AGEMM_EPOCH_BASE (the testing hook that starts the epoch counters near their wrap)
+    is checked before anything is allocated: a value that is not a number in 0..2^32-1
+    makes both context kinds return EINVAL, with no device involved."""
+    lib = agemm.load()
+    monkeypatch.setenv("AGEMM_EPOCH_BASE", value)
+    h = ctypes.c_void_p()
+    assert lib.agemm_create(ctypes.byref(h), 8, 4, 8192, 256, agemm.F16, 0) == agemm.EINVAL
+    assert not h.value
+    assert lib.fdc_create(ctypes.byref(h), 8, 96, 128, 16, agemm.F16) == agemm.EINVAL
+    assert not h.value
+    # a valid value passes the check: the shape check that follows still runs
+    monkeypatch.setenv("AGEMM_EPOCH_BASE", str(2**32 - 3))
+    assert lib.agemm_create(ctypes.byref(h), 8, 1, 512, 250, agemm.F16, 0) == agemm.ESHAPE
+
+
 def test_null_context_is_rejected():
     lib = agemm.load()
     assert lib.agemm_run_fused(None, None, None, None) == agemm.EINVAL
