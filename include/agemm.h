@@ -112,7 +112,8 @@ typedef struct {
  *                            Default: 1 for M <= 128, 2 for M <= 256, else 0
  *   AGEMM_SPLIT=0|1          MFMA work split: 0 whole tiles only, 1 the stream-K
  *                            split whenever W >= 2 (default: the split when whole
- *                            tiles would leave at least half of the CUs idle)
+ *                            tiles would leave at least half of the CUs idle and
+ *                            it saves the busiest workgroup 4096 columns of K)
  *   AGEMM_SMALL_M_MAX=0..8   largest M for which the small-M kernel is used
  *                            (default 1; 0: never)
  *   AGEMM_SMALL_M_PLAN=l,r,w small-M work split: lanes, K-ranges, workgroups per CU
@@ -143,12 +144,14 @@ int agemm_consumer_kernel(const agemm_ctx* ctx, int32_t* kind, int32_t* tile_con
  * makes): *cfg = tile configuration 0..2, *grid = workgroups of the
  * persistent grid, *split = 1 for the stream-K split. tile_config -1 and
  * split_mode -1 are the automatic choices (AGEMM_TILE_CONFIG / AGEMM_SPLIT
- * give the others). Applies to the MFMA consumer only (a context with
- * M = 1 uses the small-M kernel by default). EINVAL for M < 1, N < 8, W outside
- * 1..16, num_cus < 1 or an out-of-range tile_config / split_mode. Output
- * pointers may be NULL. */
-int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
-                    int32_t* grid, int32_t* split);
+ * give the others); the automatic split needs whole tiles to leave half of
+ * the CUs idle and the split to save the busiest workgroup at least 4096
+ * columns of K. Applies to the MFMA consumer only (a context with M = 1 uses
+ * the small-M kernel by default). EINVAL for M < 1, N < 8, W outside 1..16,
+ * K not a positive multiple of W, num_cus < 1 or an out-of-range tile_config
+ * / split_mode. Output pointers may be NULL. */
+int agemm_mfma_plan(int64_t M, int64_t N, int64_t K, int W, int num_cus, int tile_config, int split_mode,
+                    int32_t* cfg, int32_t* grid, int32_t* split);
 
 /* Everything the context's consumer launches are built from (fixed at create
  * time, except where the order set by agemm_set_order changes it, as noted).

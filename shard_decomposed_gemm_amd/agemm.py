@@ -60,7 +60,7 @@ def load() -> ctypes.CDLL:
     lib.agemm_tiles.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_consumer_kernel.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_consumer_grid.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
-    lib.agemm_mfma_plan.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    lib.agemm_mfma_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.agemm_produce.argtypes = [vp, vp, ctypes.POINTER(Schedule), vp]
     lib.agemm_run_fused.argtypes = [vp, vp, vp, vp]
@@ -89,10 +89,10 @@ def load() -> ctypes.CDLL:
     return lib
 
 
-def mfma_plan(M: int, N: int, W: int, num_cus: int, tile_config: int = -1, split_mode: int = -1):
+def mfma_plan(M: int, N: int, K: int, W: int, num_cus: int, tile_config: int = -1, split_mode: int = -1):
     """Host-only plan of the MFMA consumer (agemm_mfma_plan): (tile config, grid, split)."""
     cfg, grid, split = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    rc = load().agemm_mfma_plan(int(M), int(N), int(W), int(num_cus), int(tile_config), int(split_mode),
+    rc = load().agemm_mfma_plan(int(M), int(N), int(K), int(W), int(num_cus), int(tile_config), int(split_mode),
                                 ctypes.byref(cfg), ctypes.byref(grid), ctypes.byref(split))
     if rc != OK:
         raise AgemmError(rc, f"agemm_mfma_plan: {status_string(rc)}")

@@ -284,7 +284,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   if (!small) {
     int split_mode = -1;
     if (const char* env = std::getenv("AGEMM_SPLIT")) split_mode = std::atoi(env) != 0 ? 1 : 0;
-    c->mplan = mfma_plan(M, N, W, c->num_cus, c->tile_config, split_mode);
+    c->mplan = mfma_plan(M, N, K, W, c->num_cus, c->tile_config, split_mode);
   }
   const size_t ws_bytes = small ? sizeof(float) * (size_t)c->small_plan.ranges * (size_t)M * (size_t)N : 0;
   const size_t cnt_bytes = small ? sizeof(uint32_t) * (size_t)c->small_plan.nblk : 0;
@@ -388,7 +388,8 @@ int agemm_consumer_info(const agemm_ctx* ctx, agemm_consumer_desc* out) {
     const MfmaPlan& p = ctx->mplan;
     // arrival order runs whole tiles with the default B policy
     const bool arrival = ctx->order == AGEMM_ORDER_ARRIVAL;
-    const MfmaPlan q = arrival && p.split ? mfma_plan(ctx->M, ctx->N, ctx->W, ctx->num_cus, ctx->tile_config, 0) : p;
+    const MfmaPlan q =
+        arrival && p.split ? mfma_plan(ctx->M, ctx->N, ctx->K, ctx->W, ctx->num_cus, ctx->tile_config, 0) : p;
     d.kind = 0;
     d.tile_config = q.cfg;
     d.block_m = (int32_t)q.bm;
@@ -404,12 +405,12 @@ int agemm_consumer_info(const agemm_ctx* ctx, agemm_consumer_desc* out) {
   return AGEMM_OK;
 }
 
-int agemm_mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
+int agemm_mfma_plan(int64_t M, int64_t N, int64_t K, int W, int num_cus, int tile_config, int split_mode, int32_t* cfg,
                     int32_t* grid, int32_t* split) {
-  if (M < 1 || N < 8 || W < 1 || W > kMaxShards || num_cus < 1 || tile_config < -1 ||
+  if (M < 1 || N < 8 || W < 1 || W > kMaxShards || K < W || K % W || num_cus < 1 || tile_config < -1 ||
       tile_config >= mfma_config_count() || split_mode < -1 || split_mode > 1)
     return AGEMM_EINVAL;
-  const MfmaPlan p = mfma_plan(M, N, W, num_cus, tile_config, split_mode);
+  const MfmaPlan p = mfma_plan(M, N, K, W, num_cus, tile_config, split_mode);
   if (cfg) *cfg = p.cfg;
   if (grid) *grid = (int32_t)p.grid;
   if (split) *split = p.split ? 1 : 0;

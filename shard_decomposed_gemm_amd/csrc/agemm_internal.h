@@ -154,8 +154,8 @@ hipError_t launch_produce(const ProduceArgs& a, int max_workgroups, hipStream_t 
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 int mfma_config_count();
 int mfma_config_for(int64_t M, int tile_config);  // configuration launch_gemm_mfma uses
-// split_mode: -1 = split when it shortens the busiest workgroup's run, 0 = never, 1 = whenever W >= 2.
-MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode);
+// split_mode: -1 = split when it shortens the busiest workgroup's run enough, 0 = never, 1 = whenever W >= 2.
+MfmaPlan mfma_plan(int64_t M, int64_t N, int64_t K, int W, int num_cus, int tile_config, int split_mode);
 hipError_t launch_gemm_small_m(const SmallMArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t = {});
 // Overlap probe (probes.hip): times[0..1] = start, end of a kernel that sleeps
 // `ticks` on `first`; times[2] = start of a kernel launched after it on `second`.

@@ -809,7 +809,11 @@ int mfma_config_for(int64_t M, int tile_config) {
   return M <= 128 ? 1 : M <= 256 ? 2 : 0;
 }
 
-MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, int split_mode) {
+// A split must save the busiest workgroup at least this many columns of K
+// (see mfma_plan).
+constexpr int64_t kMinSplitSavedColumns = 4096;
+
+MfmaPlan mfma_plan(int64_t M, int64_t N, int64_t K, int W, int num_cus, int tile_config, int split_mode) {
   MfmaPlan p;
   p.cfg = mfma_config_for(M, tile_config);
   p.bm = p.cfg == 1 ? 128 : 256;
@@ -822,13 +826,23 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, in
   // that hand-off outweighs a 12.5 % shorter run (224 tiles on 256 CUs: 120
   // against 101 us at M = 128, 333 against 245 us at M = 512). The automatic
   // choice therefore splits only when whole tiles would leave at least half
-  // of the CUs idle, where the run shrinks by 2x or more.
+  // of the CUs idle, where the run shrinks by 2x or more, and only when that
+  // saves the busiest workgroup at least kMinSplitSavedColumns columns of K:
+  // the hand-off costs a fixed 18-30 us with 128-column tiles and about 95 us
+  // with 256x256 tiles. Consumer alone, W = 8 (whole against split, us):
+  //   M, N        K = 2048      K = 4096      K = 8192
+  //   8, 256      18.2 / 20.0   27.8 / 21.3   46.5 / 23.8
+  //   128, 4096   20.3 / 33.0   30.1 / 36.2   50.6 / 42.1
+  //   300, 1032   45.5 / 104.8  78.7 / 110.0  144.2 / 119.4
+  // (columns saved: 7 x K/8, i.e. 1792, 3584, 7168).
   const int64_t g_tiles = std::min<int64_t>(p.tiles, num_cus);
   const int64_t run_tiles = (p.tiles + g_tiles - 1) / g_tiles * W;
   const int64_t units = p.tiles * W;
   const int64_t g_units = std::min<int64_t>(units, num_cus);
   const int64_t run_units = (units + g_units - 1) / g_units;
-  if (split_mode < 0) p.split = W >= 2 && 2 * p.tiles <= num_cus && 2 * run_units <= run_tiles;
+  const int64_t saved_columns = (run_tiles - run_units) * (K / W);
+  if (split_mode < 0)
+    p.split = W >= 2 && 2 * p.tiles <= num_cus && 2 * run_units <= run_tiles && saved_columns >= kMinSplitSavedColumns;
   else p.split = split_mode > 0 && W >= 2;
   p.grid = p.split ? g_units : g_tiles;
   // One row block: every element of B is read by one tile only, so its loads
@@ -847,7 +861,7 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int W, int num_cus, int tile_config, in
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
   // Arrival order runs on whole tiles (a split tile's partial ranges stay in shard order).
-  MfmaPlan p = mfma_plan(a.M, a.N, a.W, a.num_cus, a.tile_config, (a.split && !arrival_requested(a)) ? 1 : 0);
+  MfmaPlan p = mfma_plan(a.M, a.N, a.K, a.W, a.num_cus, a.tile_config, (a.split && !arrival_requested(a)) ? 1 : 0);
   if (p.split && (!a.split_ws || !a.split_cnt)) return hipErrorInvalidValue;
   switch (p.cfg) {
     case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 128x128 per wave

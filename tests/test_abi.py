@@ -157,7 +157,7 @@ def test_plain_c_program_links_and_calls_the_library(tmp_path):
         "#include <stdio.h>\n#include \"agemm.h\"\n#include \"fdcombine.h\"\n"
         "int main(void) {\n"
         "  int32_t cfg = -9, grid = -9, split = -9;\n"
-        "  int rc = agemm_mfma_plan(4096, 28672, 8, 256, -1, -1, &cfg, &grid, &split);\n"
+        "  int rc = agemm_mfma_plan(4096, 28672, 8192, 8, 256, -1, -1, &cfg, &grid, &split);\n"
         "  printf(\"%s %d %d %d\\n\", agemm_status_string(rc), cfg, grid, split);\n"
         "  agemm_ctx* ctx = 0;\n"
         "  printf(\"%s\\n\", agemm_status_string(agemm_create(&ctx, 8, 4, 8192 + 8, 256, AGEMM_F16, 0)));\n"

@@ -43,15 +43,17 @@ def _paths(ctx, dsh, B, c_dtype, schedule):
     return out
 
 
-@pytest.mark.parametrize("M,N,split", [(128, 28672, False), (512, 28672, False), (4096, 28672, False),
-                                       (128, 4096, True), (512, 2048, True)])
-def test_plan(M, N, split):
-    """The automatic choice at K = 8192, W = 8: the workloads' 224 and 1792 tiles keep
-    whole tiles (224 tiles on 256 CUs: the hand-off of the partials costs more than the
-    shorter run); 32 tiles (M = 128, N = 4096) and 16 tiles (M = 512, N = 2048) split,
-    over one workgroup per CU or one per (tile, shard) unit if there are fewer."""
+@pytest.mark.parametrize("M,N,K,split", [(128, 28672, 8192, False), (512, 28672, 8192, False),
+                                         (4096, 28672, 8192, False), (128, 4096, 8192, True),
+                                         (512, 2048, 8192, True), (128, 4096, 2048, False), (8, 256, 512, False)])
+def test_plan(M, N, K, split):
+    """The automatic choice at W = 8: the workloads' 224 and 1792 tiles keep whole tiles
+    (224 tiles on 256 CUs: the hand-off of the partials costs more than the shorter run);
+    at K = 8192, 32 tiles (M = 128, N = 4096) and 16 tiles (M = 512, N = 2048) split, over
+    one workgroup per CU or one per (tile, shard) unit if there are fewer; at K = 2048 and
+    on the tiny workload the split would save too little of K and whole tiles stay."""
     import torch
-    ctx = _ctx(8, M, 8192, N, "f16")
+    ctx = _ctx(8, M, K, N, "f16")
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     assert ctx.consumer[0] == "mfma"
     assert ctx.split is split
@@ -166,12 +168,12 @@ def test_split_back_to_back_calls_reuse_counters(monkeypatch):
 
 
 def test_arrival_order_on_a_split_context_runs_whole_tiles(monkeypatch):
-    """A context that chose the split (10 tiles) asked for arrival order: those fused
+    """A context that runs the split (10 tiles) asked for arrival order: those fused
     calls run on whole tiles in arrival order, bit-exact against the oracle on exact
     inputs, with tiles released out of order into a poisoned inbox; shard-order calls
     on the same context still split."""
     import torch
-    monkeypatch.delenv("AGEMM_SPLIT", raising=False)
+    monkeypatch.setenv("AGEMM_SPLIT", "1")
     W, M, K, N = 8, 300, 2048, 1032
     a = gu.coarse_bits(0xF700 + M, M, K)
     b = gu.coarse_bits(0xF800 + N, K, N)
