@@ -175,7 +175,8 @@ def test_default_consumer_by_m(monkeypatch):
 
 @pytest.mark.parametrize("M", [1, 8, 200, 512])
 def test_structural_closed_forms(M):
-    """One-hot rows select B rows; A living in one shard sees only that shard's B rows."""
+    """One-hot rows select B rows; A living in one shard sees only that shard's B rows;
+    B of ones gives every column the row sums of A; A = 0 gives C = 0."""
     import torch
     W, K, N = 8, 2048, 776
     KS = K // W
@@ -204,6 +205,13 @@ def test_structural_closed_forms(M):
     _run(ctx, "fused", [gu.to_dev(s) for s in sh2], B, C2)
     ref = oracle.shard_partial(sh2, b, 3)
     assert np.abs(C2.cpu().numpy().astype(np.float64) - ref).max() <= oracle.tolerance(K)
+    # B = 1 -> C[m, n] = sum_k A[m, k] for every n (exact: A on a 1/16 grid, |sum| <= K)
+    a4 = gu.coarse_bits(0xD1D1, M, K)
+    ones = np.full((K, N), one, dtype=np.uint16)
+    C4 = gu.empty_c(M, N, "f32")
+    _run(ctx, "fused", [gu.to_dev(s) for s in synth.shards(a4, W)], gu.to_dev(ones), C4)
+    rows = a4.view(np.float16).astype(np.float64).sum(axis=1)
+    assert np.array_equal(C4.cpu().numpy().astype(np.float64), np.repeat(rows[:, None], N, axis=1))
     # A = 0 -> C = 0
     C3 = gu.empty_c(M, N, "f32")
     _run(ctx, "fused", [torch.zeros((M, KS), dtype=torch.float16, device=gu.dev()) for _ in range(W)], B, C3)
