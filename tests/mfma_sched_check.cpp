@@ -359,6 +359,11 @@ int main(int argc, char** argv) {
   list.push_back({256, 28672, 8, 128, 128, cfgs[0], 256, true});
   list.push_back({256, 28672, 8, 128, 128, cfgs[2], 224, false});
   list.push_back({192, 28672, 8, 128, 128, cfgs[2], 224, false});
+  // the accepted size limits (32-bit lane offsets): N = 2^24 with one shard of
+  // 64 columns (131,072 one-k-step tiles), K = 2^22 with W = 8 (split and whole)
+  list.push_back({2, 1 << 24, 1, 64, 64, cfgs[1], 256, false});
+  list.push_back({3, 136, 8, 1 << 19, 1 << 16, cfgs[1], 16, true});
+  list.push_back({3, 136, 8, 1 << 19, 1 << 16, cfgs[0], 1, false});
   while ((int)list.size() < budget) {
     Shape s;
     s.cfg = cfgs[rng() % 3];
