@@ -514,11 +514,23 @@ def main():
     wall_timed = time.perf_counter() - t1
     kern_us = ctx.timing_end()
     ctx.check()
+    # ---- a third pass with a timing event recorded on the consumer stream after each
+    # step: the spacing of consecutive step ends gives each step's time (median and
+    # spread) beside the mean of the first pass.
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ends[0].record(sc)
+    for i in range(args.steps):
+        fused_step(i)
+        ends[i + 1].record(sc)
+    torch.cuda.synchronize()
+    ctx.check()
+    step_us = np.array([ends[i].elapsed_time(ends[i + 1]) * 1e3 for i in range(args.steps)])
     ms_step = wall * 1e3 / args.steps
     flops, cons_bytes, path_bytes = algorithmic(W, M, K, N, c_bytes)
     value = flops / (ms_step * 1e-3) / 1e12
     kavg = float(np.mean(kern_us)) * 1e-3  # ms
-    print(f"[bench] fused: {ms_step * 1e3:.1f} us/step ({wall_timed * 1e6 / args.steps:.1f} with kernel timing), "
+    print(f"[bench] fused: {ms_step * 1e3:.1f} us/step ({wall_timed * 1e6 / args.steps:.1f} with kernel timing; "
+          f"step p10/p50/p90 {'/'.join('%.1f' % x for x in np.percentile(step_us, [10, 50, 90]))}), "
           f"consumer kernel {kavg * 1e3:.1f} us avg over {len(kern_us)} launches", file=sys.stderr, flush=True)
 
     mfma_bound = flops / (PEAK_FP16_TFLOPS * 1e12) > cons_bytes / (PEAK_HBM_GBS * 1e9)
@@ -604,6 +616,9 @@ def main():
         "prewarm_ms": args.prewarm_ms,
         "ms_per_step": ms_step,
         "ms_per_step_with_kernel_timing": wall_timed * 1e3 / args.steps,
+        "step_us_p10_p50_p90": [float(x) for x in np.percentile(step_us, [10, 50, 90])],
+        "step_timing": "spacing of timing events recorded on the consumer stream after each step, a third "
+                       "pass of the same steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
