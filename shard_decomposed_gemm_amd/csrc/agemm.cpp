@@ -37,7 +37,7 @@ struct agemm_ctx {
   // producer of epoch e only has to wait for the consumers of epoch e-2, so it
   // can fill its inbox while the consumer of epoch e-1 is still running.
   _Float16* inbox[2] = {nullptr, nullptr};  // each W slots of M x KS
-  uint32_t* ctrl = nullptr;      // flags[2][64] | t0 fused[2] (u64) | t0 bsp[2] (u64)
+  uint32_t* ctrl = nullptr;      // flags[2][64] | 8 u64: t0 fused[2], t0 bsp[2], probe[3]
   uint32_t* flags[2] = {nullptr, nullptr};
   uint64_t* t0_fused = nullptr;
   uint64_t* t0_bsp = nullptr;
@@ -60,6 +60,13 @@ struct agemm_ctx {
   uint32_t epoch = 0;            // produce calls so far; epoch e uses inbox e & 1
   uint32_t slot_epochs[2] = {0, 0};  // produce calls per inbox so far
   uint32_t parity_fused = 0, parity_bsp = 0;
+  // Inbox guard: per inbox, the counters its fused consumers count their
+  // units into (device) and the totals of the launches issued on it so far
+  // (host). The producer of an inbox waits for them on the device instead of
+  // behind a stream dependency.
+  uint32_t* guard_mem = nullptr;  // both inboxes' counters, kGuardStride apart
+  uint32_t* consumed[2] = {nullptr, nullptr};
+  uint32_t guard_target[2][kGuardCounters] = {};
 
   hipStream_t pair[2] = {nullptr, nullptr};  // agemm_streams: producer, consumer (owned)
   uint64_t* probe_times = nullptr;           // 3 words in ctrl for the overlap probe
@@ -116,8 +123,11 @@ int order_after_consumer(agemm_ctx* c, hipStream_t s) {
   return e == hipSuccess ? AGEMM_OK : hip_fail(c, e, "hipStreamWaitEvent");
 }
 
-// Launches the GEMM (a4-a6 of the path) with the given A source and gate.
-int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* B, void* C, hipStream_t s) {
+// Launches the GEMM (a4-a6 of the path) with the given A source and gate. A
+// fused launch also gets its inbox's guard counters (`consumed`) and adds the
+// units it counts into them to their totals (`target`) once launched.
+int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* B, void* C, hipStream_t s,
+                uint32_t* consumed = nullptr, uint32_t (*target)[kGuardCounters] = nullptr) {
   GemmArgs g{};
   g.a = src;
   g.B = static_cast<const _Float16*>(B);
@@ -134,6 +144,7 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
   g.arrival = (gate.flags != nullptr && c->order == AGEMM_ORDER_ARRIVAL) ? 1 : 0;
   g.split_ws = c->mws;
   g.split_cnt = c->mcnt;
+  g.consumed = consumed;
   const bool f32 = c->c_dtype == AGEMM_F32;
   const LaunchTiming t = c->timer.next();
   hipError_t e;
@@ -144,8 +155,10 @@ int launch_gemm(agemm_ctx* c, const ASource& src, const Gate& gate, const void* 
     sa.ws = c->ws;
     sa.counters = c->counters;
     e = launch_gemm_small_m(sa, f32, s, t);
+    if (e == hipSuccess && target) add_guard_units(*target, small_m_guard_units(c->small_plan));
   } else {
     e = launch_gemm_mfma(g, f32, s, t);
+    if (e == hipSuccess && target) add_guard_units(*target, mfma_guard_units(g));
   }
   if (e != hipSuccess) return hip_fail(c, e, "kernel launch");
   return AGEMM_OK;
@@ -167,6 +180,7 @@ void free_all(agemm_ctx* c) {
   if (c->gathered) (void)hipFree(c->gathered);
   if (c->ws) (void)hipFree(c->ws);
   if (c->counters) (void)hipFree(c->counters);
+  if (c->guard_mem) (void)hipFree(c->guard_mem);
   if (c->mws) (void)hipFree(c->mws);
   if (c->mcnt) (void)hipFree(c->mcnt);
   if (c->err_host) (void)hipHostFree(c->err_host);
@@ -266,6 +280,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
   const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 8 * sizeof(uint64_t);  // + probe times
+  const size_t guard_bytes = sizeof(uint32_t) * 2 * kGuardCounters * kGuardStride;
   int small_max = small_m_default_max();
   if (const char* env = std::getenv("AGEMM_SMALL_M_MAX")) {
     const int v = std::atoi(env);
@@ -291,6 +306,8 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   bool ok = hipMalloc(&c->inbox[0], 2 * inbox_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->gathered, gathered_bytes) == hipSuccess;
   ok = ok && hipMalloc(&c->ctrl, ctrl_bytes) == hipSuccess;
+  ok = ok && hipMalloc(&c->guard_mem, guard_bytes) == hipSuccess;
+  ok = ok && hipMemset(c->guard_mem, 0, guard_bytes) == hipSuccess;
   if (ok && small) {
     ok = hipMalloc(&c->ws, ws_bytes) == hipSuccess;
     ok = ok && hipMalloc(&c->counters, cnt_bytes) == hipSuccess;
@@ -312,6 +329,8 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   c->t0_fused = reinterpret_cast<uint64_t*>(c->ctrl + 2 * kMaxTiles);
   c->t0_bsp = c->t0_fused + 2;
   c->probe_times = c->t0_bsp + 2;
+  c->consumed[0] = c->guard_mem;
+  c->consumed[1] = c->guard_mem + kGuardCounters * kGuardStride;
   void* hp = nullptr;
   e = hipMemset(c->ctrl, 0, ctrl_bytes);
   if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);
@@ -327,6 +346,15 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
     c->slot_epochs[0] = c->slot_epochs[1] = base;
     const std::vector<uint32_t> init(2 * kMaxTiles, base * (uint32_t)c->items_per_tile);
     e = hipMemcpy(c->ctrl, init.data(), init.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) {
+      // the inbox guard's counters and their totals start there too
+      std::vector<uint32_t> counts(guard_bytes / sizeof(uint32_t), 0u);
+      for (int j = 0; j < 2 * kGuardCounters; ++j) {
+        counts[(size_t)j * kGuardStride] = base;
+        c->guard_target[j / kGuardCounters][j % kGuardCounters] = base;
+      }
+      e = hipMemcpy(c->guard_mem, counts.data(), guard_bytes, hipMemcpyHostToDevice);
+    }
   }
   if (e == hipSuccess) e = c->so.create();
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -429,6 +457,8 @@ int agemm_streams(agemm_ctx* ctx, void** producer, void** consumer) {
   if (!ctx->pair[0]) {
     const int rc = find_stream_pair(ctx->pair, ctx->probe_times, ctx->ticks_per_ns, &ctx->last_error);
     if (rc) return rc;
+    ctx->so.owned[0] = ctx->pair[0];  // the context's own streams: their events are recorded lazily
+    ctx->so.owned[1] = ctx->pair[1];
   }
   *producer = ctx->pair[0];
   *consumer = ctx->pair[1];
@@ -458,11 +488,17 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // This epoch's inbox may be overwritten only once the fused consumers that
-  // last read it (two epochs ago) are done; producers run in order.
+  // read it before (two epochs ago, and earlier) are done with it: the
+  // producer waits for them on the device (the inbox guard), not behind a
+  // stream dependency. Producers run in call order.
   const int slot = (int)((ctx->epoch + 1) & 1u);
-  hipError_t e = ctx->so.before_produce(slot, s);
+  hipError_t e = ctx->so.before_produce(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_produce_args(ctx, a_shards, pa);
+  pa.consumed = ctx->consumed[slot];
+  std::memcpy(pa.guard_target, ctx->guard_target[slot], sizeof pa.guard_target);  // wrap with the counters
+  pa.timeout_ticks = ctx->timeout_ticks;
+  pa.err = ctx->err_dev;
   pa.dst = ctx->inbox[slot];
   pa.dst_shard_stride = ctx->M * ctx->KS;
   pa.dst_ld = ctx->KS;
@@ -497,9 +533,9 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   gate.target = ctx->slot_epochs[slot] * (uint32_t)ctx->items_per_tile;  // wraps with the counters
   gate.timeout_ticks = ctx->timeout_ticks;
   gate.strict = ctx->strict_acquire;
-  rc = launch_gemm(ctx, src, gate, B, C, s);
+  rc = launch_gemm(ctx, src, gate, B, C, s, ctx->consumed[slot], &ctx->guard_target[slot]);
   if (rc) return rc;
-  const hipError_t e = ctx->so.after_fused(slot, s);
+  const hipError_t e = ctx->so.after_consumer(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   return AGEMM_OK;
 }
@@ -540,7 +576,7 @@ int agemm_run_bsp(agemm_ctx* ctx, const void* const* a_shards, const void* B, vo
   src.panels = ctx->a_panels;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
-  const hipError_t eo = ctx->so.after_other(s);
+  const hipError_t eo = ctx->so.after_consumer(s);
   return eo == hipSuccess ? AGEMM_OK : hip_fail(ctx, eo, "hipEventRecord");
 }
 
@@ -557,7 +593,7 @@ int agemm_run_pull(agemm_ctx* ctx, const void* const* a_shards, const void* B, v
   src.lda = ctx->KS;
   rc = launch_gemm(ctx, src, no_gate(ctx), B, C, s);
   if (rc) return rc;
-  const hipError_t eo = ctx->so.after_other(s);
+  const hipError_t eo = ctx->so.after_consumer(s);
   return eo == hipSuccess ? AGEMM_OK : hip_fail(ctx, eo, "hipEventRecord");
 }
 
@@ -575,7 +611,7 @@ int agemm_check(agemm_ctx* ctx) {
   if (!ctx) return AGEMM_EINVAL;
   volatile ErrWord* w = ctx->err_host;
   if (w->code == 0) return AGEMM_OK;
-  const unsigned tile = w->tile, target = w->target, seen = w->seen;
+  const unsigned code = w->code, tile = w->tile, target = w->target, seen = w->seen;
   w->code = 0;
   // A timed-out launch can leave split-K counters part-way; clear them.
   hipError_t e = hipSuccess;
@@ -583,6 +619,10 @@ int agemm_check(agemm_ctx* ctx) {
   if (e == hipSuccess && ctx->mcnt) e = hipMemset(ctx->mcnt, 0, ctx->mplan.cnt_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(ctx, e, "hipMemset(counters)");
+  if (code == 2)
+    return fail(ctx, AGEMM_ETIMEOUT,
+                "producer gave up waiting for the consumers of its inbox (guard counter %u at %u, target %u)", tile,
+                seen, target);
   return fail(ctx, AGEMM_ETIMEOUT, "consumer gave up waiting for tile %u (flag %u, target %u)", tile, seen, target);
 }
 

@@ -12,11 +12,23 @@ constexpr int kMaxTiles = 64;   // T = W * KT; one wave polls every flag at once
 
 // Device error word (lives in host-pinned, device-mapped memory).
 struct ErrWord {
-  uint32_t code;     // 0 = none, 1 = flag wait timed out
-  uint32_t tile;     // tile id that timed out
-  uint32_t target;   // flag value waited for
-  uint32_t seen;     // last flag value observed
+  uint32_t code;     // 0 = none, 1 = flag wait timed out, 2 = inbox guard wait timed out (producer)
+  uint32_t tile;     // tile id (code 1) or guard counter (code 2) that timed out
+  uint32_t target;   // value waited for
+  uint32_t seen;     // last value observed
 };
+
+// Inbox guard: per inbox, kGuardCounters counters into which a fused
+// consumer launch counts its units (the small-M kernel's items, the MFMA
+// kernel's workgroups: unit u into counter u % kGuardCounters) once they are
+// done reading the inbox. The producer of a later epoch on that inbox waits
+// on the device until every counter has reached the total of the launches
+// issued on it, instead of behind a stream dependency. Spreading the counts keeps each address to a few dozen
+// atomics per launch, and one counter per 4 KiB spreads the addresses over
+// the memory channels (counters on a couple of lines serialised the counts
+// and held up the consumer's stream); one wave polls all of them at once.
+constexpr int kGuardCounters = 64;
+constexpr int kGuardStride = 1024;  // uint32 elements from one counter to the next
 
 // Columns of one k-panel of the inbox layout (see ASource).
 constexpr int kPanelK = 32;
@@ -72,6 +84,9 @@ struct GemmArgs {
   // Gated launches only: 1 = take each output tile's flag tiles in arrival
   // order (raised ones first), 0 = shard order.
   int32_t arrival;
+  // Gated launches with the inbox guard: the inbox's kGuardCounters counters
+  // (kGuardStride apart) this launch counts its units into (nullptr: none).
+  uint32_t* consumed;
 };
 
 // Default flag k-tile BKf for shard width KS and W shards: min(256, KS),
@@ -120,6 +135,14 @@ struct ProduceArgs {
   int32_t items_per_tile;           // = ceil(M / rows_per_item), contributors per flag
   int32_t order[kMaxTiles];         // tile released p-th
   uint32_t offset_ticks[kMaxTiles]; // its release time after the launch's start, wall-clock ticks
+  // Inbox guard (push only; nullptr: none): before its first copy every
+  // workgroup waits until counter j of `consumed` has reached guard_target[j]
+  // (wrap-aware), the units that the fused launches issued on the inbox
+  // count into it.
+  const uint32_t* consumed;
+  uint32_t guard_target[kGuardCounters];
+  uint64_t timeout_ticks;           // bound of the guard wait
+  ErrWord* err;
 };
 
 // Work split of the small-M path, chosen on the host for the device's CU
@@ -140,6 +163,16 @@ struct SmallMArgs {
   float* ws;          // ranges x M x N partial sums
   uint32_t* counters; // one per column block, zero between calls
 };
+// Units a small-M launch counts into the inbox guard: one per item.
+inline int64_t small_m_guard_units(const SmallMPlan& p) { return (int64_t)p.ranges * p.nblk; }
+// Units an MFMA launch counts into the inbox guard: one per workgroup of the
+// grid launch_gemm_mfma uses for these arguments.
+int64_t mfma_guard_units(const GemmArgs& a);
+// Adds the shares of a launch of `units` units to the guard counters' totals.
+inline void add_guard_units(uint32_t (&target)[kGuardCounters], int64_t units) {
+  for (int j = 0; j < kGuardCounters; ++j)
+    target[j] += (uint32_t)(units / kGuardCounters + (j < units % kGuardCounters ? 1 : 0));
+}
 
 // Optional HIP events attached to a consumer kernel's dispatch (its own start
 // and end timestamps); null = plain launch.

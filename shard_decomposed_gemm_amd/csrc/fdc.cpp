@@ -225,6 +225,8 @@ int fdc_streams(fdc_ctx* ctx, void** producer, void** consumer) {
   if (!ctx->pair[0]) {
     const int rc = find_stream_pair(ctx->pair, ctx->probe_times, ctx->ticks_per_ns, &ctx->last_error);
     if (rc) return rc;
+    ctx->so.owned[0] = ctx->pair[0];  // the context's own streams: their events are recorded lazily
+    ctx->so.owned[1] = ctx->pair[1];
   }
   *producer = ctx->pair[0];
   *consumer = ctx->pair[1];
@@ -253,7 +255,7 @@ int fdc_produce(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
   // producer cost about 4 us of command-processor time per epoch (59 against
   // 55 us per step). Producers stay in call order.
   const int slot = (int)((ctx->epoch + 1) & 1u);
-  hipError_t e = ctx->so.after_last_producer(s);
+  hipError_t e = ctx->so.before_produce(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_args(ctx, o_parts, lse_parts, pa);
   pa.dst = ctx->inbox[slot];
@@ -289,7 +291,7 @@ int fdc_run_fused(fdc_ctx* ctx, void* O, void* stream) {
   int rc = launch_combine(ctx, ctx->inbox[slot], ctx->flags[slot], ctx->slot_epochs[slot], ctx->consumed[slot], O, s);
   if (rc) return rc;
   ctx->fused_issued[slot]++;
-  e = ctx->so.after_fused(slot, s);
+  e = ctx->so.after_consumer(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   return AGEMM_OK;
 }
@@ -325,7 +327,7 @@ int fdc_run_bsp(fdc_ctx* ctx, const void* const* o_parts, const void* const* lse
   // 3) the same combine with the flags off
   rc = launch_combine(ctx, ctx->gathered, nullptr, 0, nullptr, O, s);
   if (rc) return rc;
-  e = ctx->so.after_other(s);
+  e = ctx->so.after_consumer(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   return AGEMM_OK;
 }

@@ -727,6 +727,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
   };
   main_loop();
   __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (GATED) {
+    // Inbox guard: every load of the workgroup, its inbox reads among them,
+    // has completed (each wave's wait above; then the barrier); count the
+    // workgroup out of the inbox (no returned value).
+    if (g.consumed != nullptr) {
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(g.consumed + (int)(blockIdx.x % kGuardCounters) * kGuardStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 inline bool arrival_requested(const GemmArgs& a) { return a.arrival != 0 && a.gate.flags != nullptr; }
@@ -859,9 +870,15 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int64_t K, int W, int num_cus, int tile
   return p;
 }
 
+// Arrival order runs on whole tiles (a split tile's partial ranges stay in shard order).
+static MfmaPlan launch_plan(const GemmArgs& a) {
+  return mfma_plan(a.M, a.N, a.K, a.W, a.num_cus, a.tile_config, (a.split && !arrival_requested(a)) ? 1 : 0);
+}
+
+int64_t mfma_guard_units(const GemmArgs& a) { return launch_plan(a).grid; }
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool out_f32, hipStream_t s, const LaunchTiming& t) {
-  // Arrival order runs on whole tiles (a split tile's partial ranges stay in shard order).
-  MfmaPlan p = mfma_plan(a.M, a.N, a.K, a.W, a.num_cus, a.tile_config, (a.split && !arrival_requested(a)) ? 1 : 0);
+  MfmaPlan p = launch_plan(a);
   if (p.split && (!a.split_ws || !a.split_cnt)) return hipErrorInvalidValue;
   switch (p.cfg) {
     case 0: return launch_cfg<256, 256, 32, 4, 2, 2>(a, p, out_f32, s, t);   // 4 waves, 128x128 per wave

@@ -28,7 +28,10 @@
 // stream at HBM speed.
 // Partial sums go to a workspace per K-range; the last workgroup of a column
 // block (counted with an atomic) adds the R partials in range order and writes
-// C. The result does not depend on arrival order.
+// C. The result does not depend on arrival order. In a fused launch each item
+// is also counted out of the inbox at its end (the inbox guard, see the
+// producer), so the producer of a later epoch may overwrite the inbox without
+// a stream dependency.
 #include "agemm_internal.h"
 
 namespace agemm {
@@ -264,6 +267,16 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(SmallMArgs sa) {
     if (tid == 0) {
       const uint32_t old = __hip_atomic_fetch_add(sa.counters + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (old == (uint32_t)(R - 1));
+      // Inbox guard: every wave of the item has waited for all its loads
+      // above, the A copies from the inbox long among them; count the item
+      // out of the inbox (item i into counter i % kGuardCounters; no returned
+      // value). Counting right after the copies instead, mid-item, put the
+      // atomic in front of the stream's load waits and cost 2 us per launch.
+      if constexpr (GATED) {
+        if (g.consumed != nullptr)
+          __hip_atomic_fetch_add(g.consumed + (item % kGuardCounters) * kGuardStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(s_last)) continue;

@@ -103,65 +103,55 @@ int find_stream_pair(hipStream_t pair[2], uint64_t* probe_times, double ticks_pe
 
 hipError_t StreamOrder::create() {
   hipError_t e = hipEventCreateWithFlags(&ev_producer, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_other, hipEventDisableTiming);
-  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ev_fused[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_consumer, hipEventDisableTiming);
   return e;
 }
 
 void StreamOrder::destroy() {
   if (ev_producer) (void)hipEventDestroy(ev_producer);
-  if (ev_other) (void)hipEventDestroy(ev_other);
-  for (int i = 0; i < 2; ++i)
-    if (ev_fused[i]) (void)hipEventDestroy(ev_fused[i]);
-  ev_producer = ev_other = ev_fused[0] = ev_fused[1] = nullptr;
+  if (ev_consumer) (void)hipEventDestroy(ev_consumer);
+  ev_producer = ev_consumer = nullptr;
 }
 
-hipError_t StreamOrder::before_produce(int slot, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  if (fused_pending[slot] && fused_stream[slot] != s) e = hipStreamWaitEvent(s, ev_fused[slot], 0);
-  if (e == hipSuccess && producer_pending && producer_stream != s) e = hipStreamWaitEvent(s, ev_producer, 0);
-  return e;
+// Makes s wait for the last call marked on `from` (recording its event now if
+// that was put off).
+hipError_t StreamOrder::wait_for(hipEvent_t ev, hipStream_t from, bool pending, bool* recorded, hipStream_t s) {
+  if (!pending || from == s) return hipSuccess;
+  if (!*recorded) {
+    const hipError_t e = hipEventRecord(ev, from);
+    if (e != hipSuccess) return e;
+    *recorded = true;
+  }
+  return hipStreamWaitEvent(s, ev, 0);
 }
 
-hipError_t StreamOrder::after_last_producer(hipStream_t s) {
-  if (producer_pending && producer_stream != s) return hipStreamWaitEvent(s, ev_producer, 0);
+// Marks a call made on s: records its event now, or puts the record off.
+hipError_t StreamOrder::mark(hipEvent_t ev, hipStream_t s, bool lazy, hipStream_t* stream, bool* pending,
+                             bool* recorded) {
+  if (!lazy) {
+    const hipError_t e = hipEventRecord(ev, s);
+    if (e != hipSuccess) return e;
+  }
+  *stream = s;
+  *pending = true;
+  *recorded = !lazy;
   return hipSuccess;
+}
+
+hipError_t StreamOrder::before_produce(hipStream_t s) {
+  return wait_for(ev_producer, producer_stream, producer_pending, &producer_recorded, s);
 }
 
 hipError_t StreamOrder::after_produce(hipStream_t s) {
-  const hipError_t e = hipEventRecord(ev_producer, s);
-  if (e == hipSuccess) {
-    producer_pending = true;
-    producer_stream = s;
-  }
-  return e;
+  return mark(ev_producer, s, is_owned(s), &producer_stream, &producer_pending, &producer_recorded);
 }
 
 hipError_t StreamOrder::before_consumer(hipStream_t s) {
-  if (consumer_pending && consumer_stream != s) return hipStreamWaitEvent(s, last_consumer, 0);
-  return hipSuccess;
+  return wait_for(ev_consumer, consumer_stream, consumer_pending, &consumer_recorded, s);
 }
 
-hipError_t StreamOrder::after_fused(int slot, hipStream_t s) {
-  const hipError_t e = hipEventRecord(ev_fused[slot], s);
-  if (e == hipSuccess) {
-    fused_pending[slot] = true;
-    fused_stream[slot] = s;
-    last_consumer = ev_fused[slot];
-    consumer_stream = s;
-    consumer_pending = true;
-  }
-  return e;
-}
-
-hipError_t StreamOrder::after_other(hipStream_t s) {
-  const hipError_t e = hipEventRecord(ev_other, s);
-  if (e == hipSuccess) {
-    last_consumer = ev_other;
-    consumer_stream = s;
-    consumer_pending = true;
-  }
-  return e;
+hipError_t StreamOrder::after_consumer(hipStream_t s) {
+  return mark(ev_consumer, s, is_owned(s), &consumer_stream, &consumer_pending, &consumer_recorded);
 }
 
 int KernelTimer::begin(int32_t max_launches, std::string* last) {

@@ -24,6 +24,15 @@
 // schedule makes an item wait until offset_ticks[p] after a start time
 // shared by all workgroups of the launch; offsets do not decrease with p, so
 // a workgroup never holds a later item behind an earlier one's delay.
+//
+// The inbox is guarded on the device: before its first copy, every workgroup waits until the fused consumers that read this
+// inbox in earlier epochs have counted themselves out of it (wave 0 polls the
+// kGuardCounters counters, one lane each, sleeping long between looks). A
+// consumer wave counts itself out only after its inbox reads have returned,
+// so the stores below cannot overtake them. The wait replaces a stream
+// dependency, whose command-processor work sat between consecutive consumer
+// launches (with the record after each consumer that it waits for, about
+// 3 us per step at M = 1).
 #include "agemm_internal.h"
 
 namespace agemm {
@@ -45,6 +54,34 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
 template <bool FLAGS>
 __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a) {
   const int items = a.t * a.items_per_tile;
+  if constexpr (FLAGS) {
+    if (a.consumed != nullptr) {
+      if (threadIdx.x < kGuardCounters) {
+        const int j = threadIdx.x;
+        const uint32_t target = a.guard_target[j];  // wraps with the counter
+        const uint64_t start = wall_clock();
+        while (true) {
+          const uint32_t v = __hip_atomic_load(const_cast<uint32_t*>(a.consumed) + j * kGuardStride,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t behind = __ballot((int32_t)(v - target) < 0);
+          if (behind == 0) break;
+          if (wall_clock() - start > a.timeout_ticks) {
+            if (j == __builtin_ctzll(behind)) {
+              __hip_atomic_store(&a.err->tile, (uint32_t)j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+              __hip_atomic_store(&a.err->target, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+              __hip_atomic_store(&a.err->seen, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+              __hip_atomic_store(&a.err->code, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+            break;
+          }
+          // about 4 us between looks: the consumers it waits for run for tens
+          // of microseconds, and the looks should not load one memory channel
+          __builtin_amdgcn_s_sleep(127);
+        }
+      }
+      __syncthreads();
+    }
+  }
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int p = item / a.items_per_tile;
     const int q = item - p * a.items_per_tile;

@@ -57,3 +57,17 @@ def pick_consumer(monkeypatch, kernel):
 def assert_consumer(ctx, kernel):
     if kernel is not None:
         assert ctx.consumer_info()["kind"] == kernel, ctx.consumer_info()
+
+
+def hold_stream(stream, ms: float):
+    """Queues on `stream` a one-wave spin kernel (torch.cuda._sleep) that delays the
+    stream's later work by at least `ms` milliseconds without occupying the CUs: it
+    spins for ms x 2.4e6 engine-clock cycles, and the part's engine clock never exceeds
+    2.4 GHz (at a lower clock the hold is longer). Returns timing events around it."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record()
+        torch.cuda._sleep(int(ms * 2.4e6))
+        end.record()
+    return start, end

@@ -215,10 +215,10 @@ def test_fd_epochs_across_the_counter_wrap(monkeypatch):
 
 
 def test_fd_inbox_guard_holds_the_producer_for_a_late_combine():
-    """The combine of epoch 0 starts late (its stream first runs a long matrix product),
-    after the producers of epochs 1 and 2 were issued. Epoch 2 reuses epoch 0's inbox:
-    its producer must wait on the device until that combine has read it, so every
-    epoch's output still matches its own partials."""
+    """The combine of epoch 0 starts late (its stream first runs a spin kernel of tens of
+    milliseconds), after the producers of epochs 1 and 2 were issued. Epoch 2 reuses epoch 0's inbox:
+    its producer must wait on the device until that combine has read it (timed: it
+    spans most of the spin), so every epoch's output still matches its own partials."""
     import torch
     W, H, D, HT = 8, 96, 128, 16
     sets = [synth.fd_partials(0x7B00 + 16 * k, W, H, D) for k in range(3)]
@@ -226,19 +226,24 @@ def test_fd_inbox_guard_holds_the_producer_for_a_late_combine():
     devs = [_dev_parts(o, l) for o, l in sets]
     ctx = _ctx(W, H, D, HT, "f32")
     sp, sc = ctx.streams()
-    x = torch.full((8192, 8192), 1e-4, device=gu.dev())
     torch.cuda.synchronize()
+    h0, h1 = gu.hold_stream(sc, 40.0)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     outs = []
-    with torch.cuda.stream(sc):
-        y = x @ x  # several milliseconds ahead of the first combine on its stream
     for k in range(3):
         O = _out(H, D, "f32")
+        if k == 2:
+            p0.record(sp)
         ctx.produce(*devs[k], stream=sp)
+        if k == 2:
+            p1.record(sp)
         ctx.run_fused(O, stream=sc)
         outs.append(O)
     torch.cuda.synchronize()
     ctx.check()
-    assert torch.isfinite(y).all()
+    held, waited = h0.elapsed_time(h1), p0.elapsed_time(p1)
+    assert held > 15.0, held
+    assert waited > 0.5 * held, (waited, held)
     for k, O in enumerate(outs):
         assert np.abs(O.cpu().numpy().astype(np.float64) - refs[k]).max() <= fdo.tolerance("f32"), k
 

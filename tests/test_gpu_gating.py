@@ -198,6 +198,160 @@ def test_timeout_reports_and_recovers(M):
     assert np.abs(gu.c_to_f64(C2) - ref).max() <= oracle.tolerance(K)
 
 
+@pytest.mark.parametrize("M,kernel", [(1, "small_m"), (130, "mfma"), (4, "mfma")])
+def test_inbox_guard_holds_the_producer_for_a_late_consumer(M, kernel):
+    """The producer waits on the device, not behind a stream dependency, until the
+    fused consumers that read its inbox before are done with it (both consumer
+    kernels count themselves out of the inbox). The consumer of the first epoch
+    starts late (its stream first runs a spin kernel of tens of milliseconds), after
+    the producers of the next two epochs were issued; the third epoch reuses the
+    first one's inbox, so its producer must hold until that consumer has read it
+    (timed: it spans most of the spin). Every epoch's C must equal its own Pull
+    result bit for bit."""
+    import torch
+    W, K, N = 8, 2048, 1544
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (71, 72, 73)]
+    ctx = _ctx(W, M, K, N, "f16")
+    gu.assert_consumer(ctx, kernel)
+    refs = []
+    for p in probs:
+        C = gu.empty_c(M, N, "f16")
+        ctx.run_pull(p[3], p[4], C)
+        refs.append(C)
+    torch.cuda.synchronize()
+    sp, sc = ctx.streams()
+    h0, h1 = gu.hold_stream(sc, 40.0)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    outs = []
+    for e in range(3):
+        C = gu.empty_c(M, N, "f16")
+        if e == 2:
+            p0.record(sp)
+        ctx.produce(probs[e][3], stream=sp)
+        if e == 2:
+            p1.record(sp)
+        ctx.run_fused(probs[e][4], C, stream=sc)
+        outs.append(C)
+    torch.cuda.synchronize()
+    ctx.check()
+    held, waited = h0.elapsed_time(h1), p0.elapsed_time(p1)
+    assert held > 15.0, held  # the consumer really started late
+    assert waited > 0.5 * held, (waited, held)  # and the producer held for it
+    for e, C in enumerate(outs):
+        assert torch.equal(C.view(torch.int16), refs[e].view(torch.int16)), e
+    ctx.close()
+
+
+@pytest.mark.parametrize("M,kernel", [(1, "small_m"), (130, "mfma")])
+def test_inbox_guard_timeout_reports_and_recovers(M, kernel):
+    """The consumer of the first epoch is held (a spin kernel of tens of milliseconds on
+    its stream) for longer than the 2 ms spin timeout, so the producer of the third epoch (same inbox)
+    gives up waiting: agemm_check reports ETIMEOUT for the producer, and later epochs are
+    correct again."""
+    import torch
+    from shard_decomposed_gemm_amd import AgemmError
+    from shard_decomposed_gemm_amd.agemm import ETIMEOUT
+    W, K, N = 8, 2048, 1024
+    a, sh, b, dsh, B = gu.random_problem(W, M, K, N, seed=62)
+    ref = oracle.sharded_gemm(sh, b)
+    ctx = _ctx(W, M, K, N, "f32")
+    gu.assert_consumer(ctx, kernel)
+    sp, sc = ctx.streams()
+    ctx.set_spin_timeout_us(2_000)
+    h0, h1 = gu.hold_stream(sc, 40.0)
+    late = [gu.empty_c(M, N, "f32") for _ in range(3)]  # kept alive until the kernels have run
+    for C in late:
+        ctx.produce(dsh, stream=sp)
+        ctx.run_fused(B, C, stream=sc)
+    torch.cuda.synchronize()
+    assert h0.elapsed_time(h1) > 15.0
+    with pytest.raises(AgemmError) as ei:
+        ctx.check()
+    assert ei.value.status == ETIMEOUT
+    assert "producer" in str(ei.value)
+    ctx.check()  # the error word is cleared
+    ctx.set_spin_timeout_us(2_000_000)
+    outs = []
+    for e in range(3):
+        C = gu.empty_c(M, N, "f32")
+        ctx.produce(dsh, stream=sp)
+        ctx.run_fused(B, C, stream=sc)
+        outs.append(C)
+    torch.cuda.synchronize()
+    ctx.check()
+    for C in outs:
+        assert np.abs(gu.c_to_f64(C) - ref).max() <= oracle.tolerance(K)
+    ctx.close()
+
+
+@pytest.mark.parametrize("M", [1, 130])
+def test_producer_order_survives_a_switch_from_the_context_streams(M):
+    """Producer events on the context's own streams are recorded only when a call on
+    another stream needs them. The first producer runs on the context's producer stream
+    behind a spin kernel of tens of milliseconds; the next two run on the default stream
+    and must still come after it. The third reuses the first one's inbox: had it
+    overtaken the first, its consumer would read the first epoch's data."""
+    import torch
+    W, K, N = 8, 2048, 1544
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (81, 82, 83)]
+    ctx = _ctx(W, M, K, N, "f16")
+    refs = []
+    for p in probs:
+        C = gu.empty_c(M, N, "f16")
+        ctx.run_pull(p[3], p[4], C)
+        refs.append(C)
+    torch.cuda.synchronize()
+    sp, sc = ctx.streams()
+    h0, h1 = gu.hold_stream(sp, 40.0)
+    ctx.produce(probs[0][3], stream=sp)
+    ctx.produce(probs[1][3])  # default stream
+    p2 = torch.cuda.Event(enable_timing=True)
+    p2.record()
+    ctx.produce(probs[2][3])
+    C = gu.empty_c(M, N, "f16")
+    ctx.run_fused(probs[2][4], C)
+    torch.cuda.synchronize()
+    ctx.check()
+    assert h0.elapsed_time(h1) > 15.0
+    assert h0.elapsed_time(p2) >= h0.elapsed_time(h1)  # the second producer ran after the held one
+    assert torch.equal(C.view(torch.int16), refs[2].view(torch.int16))
+    ctx.close()
+
+
+@pytest.mark.parametrize("M", [1, 130])
+def test_consumer_order_survives_a_switch_from_the_context_streams(M):
+    """Consumer events on the context's own streams are recorded only when a call on
+    another stream needs them. A fused consumer on the context's consumer stream waits
+    behind a spin kernel; a Pull call on the default stream, which shares the context's
+    workspaces, must still run after it, and both results stay exact."""
+    import torch
+    W, K, N = 8, 2048, 1544
+    probs = [gu.random_problem(W, M, K, N, seed=s) for s in (84, 85)]
+    ctx = _ctx(W, M, K, N, "f16")
+    refs = []
+    for p in probs:
+        C = gu.empty_c(M, N, "f16")
+        ctx.run_pull(p[3], p[4], C)
+        refs.append(C)
+    torch.cuda.synchronize()
+    sp, sc = ctx.streams()
+    ctx.produce(probs[0][3], stream=sp)
+    h0, h1 = gu.hold_stream(sc, 40.0)
+    C1 = gu.empty_c(M, N, "f16")
+    ctx.run_fused(probs[0][4], C1, stream=sc)
+    C2 = gu.empty_c(M, N, "f16")
+    ctx.run_pull(probs[1][3], probs[1][4], C2)  # default stream
+    q = torch.cuda.Event(enable_timing=True)
+    q.record()
+    torch.cuda.synchronize()
+    ctx.check()
+    assert h0.elapsed_time(h1) > 15.0
+    assert h0.elapsed_time(q) >= h0.elapsed_time(h1)  # the Pull ran after the held consumer
+    assert torch.equal(C1.view(torch.int16), refs[0].view(torch.int16))
+    assert torch.equal(C2.view(torch.int16), refs[1].view(torch.int16))
+    ctx.close()
+
+
 def test_call_order_and_argument_errors():
     import torch
     from shard_decomposed_gemm_amd import AgemmError
