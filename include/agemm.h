@@ -41,14 +41,27 @@
  * validated before anything is launched; a rejected call changes no state.
  * Calls are asynchronous on the given stream. A consumer that waits longer
  * than the spin timeout for a flag stops, records the tile in a device error
- * word and leaves C undefined; agemm_check() reports it after the caller has
- * synchronised.
+ * word and leaves C undefined; a producer that waits longer than the spin
+ * timeout for the consumers of its inbox (the inbox guard, agemm_produce)
+ * records that and copies anyway (that epoch's results are then undefined).
+ * agemm_check() reports either after the caller has synchronised.
+ *
+ * Ordering between calls on different streams: every producer comes after
+ * the previous producer of the context, every consumer call (run_fused,
+ * run_bsp, run_pull) after the previous consumer call. On the context's own
+ * streams (agemm_streams) the event a later call on another stream waits for
+ * is recorded only when that call is made, on the stream of the earlier call,
+ * so the later call may also wait for work queued there in between; on
+ * caller streams it is recorded right after each call. Destroying a caller
+ * stream is safe at any time; the context's streams live until
+ * agemm_destroy.
  *
  * Ownership: the context owns two inboxes (each W x M x KS fp16, used by
  * alternate epochs) with their flags (T uint32 counters each), the
  * gathered-A buffer of the BSP path, the split-K workspaces and the error
- * word. The caller owns A_s, B, C and all streams. Everything is allocated
- * at create time; no other call allocates.
+ * word, and the inbox guard's counters (64 per inbox, 4 KiB apart). The
+ * caller owns A_s, B, C and the streams it passes. Everything is allocated at
+ * create time; no other call allocates.
  *
  * Work split of the GEMM (fixed at create time). With few output tiles (at
  * most half as many as the GPU's compute units) whole tiles would leave most
@@ -79,7 +92,7 @@ typedef enum {
   AGEMM_ESHAPE = 2,   /* shape outside the accepted set above */
   AGEMM_ENOMEM = 3,   /* device or host allocation failed */
   AGEMM_EHIP = 4,     /* a HIP runtime call failed; see agemm_last_error */
-  AGEMM_ETIMEOUT = 5, /* a consumer gave up waiting for a flag (reported by agemm_check) */
+  AGEMM_ETIMEOUT = 5, /* a flag wait or an inbox guard wait timed out (reported by agemm_check) */
   AGEMM_ESTATE = 6    /* call out of order, e.g. run_fused before any produce */
 } agemm_status;
 
@@ -187,10 +200,13 @@ int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split);
  * raises Flags(s, kt), for every tile, in the schedule's order and at its
  * times (sched == NULL: shard order, no delay). a_shards: host array of W
  * device pointers, each M x KS fp16. Starts a new epoch: the next run_fused
- * waits for this call's flags. Epochs alternate between the two inboxes:
- * before it overwrites its inbox, the producer stream waits (device side)
- * for the last run_fused of the epoch before the previous one, so a
- * producer may fill its inbox while the previous epoch's consumer runs. */
+ * waits for this call's flags. Epochs alternate between the two inboxes.
+ * Before it overwrites its inbox the producer waits on the device (the inbox
+ * guard, no stream dependency) until every run_fused issued on that inbox so
+ * far has counted itself out of it, so a producer may fill its inbox while
+ * the previous epoch's consumer runs. That run_fused must be able to run
+ * meanwhile: on a stream the caller holds up for longer than the spin
+ * timeout, the producer gives up waiting (AGEMM_ETIMEOUT from agemm_check). */
 int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_schedule* sched, void* stream);
 
 /* Flag-gated consumer: C = sum_s Inbox(s) . B_s, waiting on Flags(s, kt)
@@ -311,8 +327,9 @@ int agemm_probe_mfma(int32_t warmup, int32_t launches, void* out, void* stream, 
 int agemm_probe_read(const void* buf, int64_t bytes, int32_t warmup, int32_t launches, void* out, void* stream,
                      double* gbs);
 
-/* After the caller has synchronised: AGEMM_ETIMEOUT if a consumer timed out
- * since the last check (the error word is then cleared), else AGEMM_OK. */
+/* After the caller has synchronised: AGEMM_ETIMEOUT if a consumer's flag wait
+ * or a producer's inbox guard timed out since the last check (the error word
+ * is then cleared; agemm_last_error says which), else AGEMM_OK. */
 int agemm_check(agemm_ctx* ctx);
 
 /* Text of the last error on this context (never NULL). */

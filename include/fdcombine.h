@@ -39,7 +39,10 @@
  * given stream (a hipStream_t passed as void*; NULL = the null stream).
  * Device-side flag waits time out after the spin timeout; fdc_check then
  * reports AGEMM_ETIMEOUT and that call's O is undefined. A context is not
- * thread-safe; use one per host thread.
+ * thread-safe; use one per host thread. Calls on different streams are
+ * ordered as in agemm.h (producer after producer, combine after combine; on
+ * the context's own streams the event a later call waits for is recorded
+ * when that call is made).
  */
 #ifndef FDCOMBINE_H_
 #define FDCOMBINE_H_

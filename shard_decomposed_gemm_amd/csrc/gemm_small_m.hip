@@ -232,6 +232,21 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(SmallMArgs sa) {
       use(X, c);
     }
 
+    // Inbox guard (thread 0, once the workgroup has passed a barrier after its
+    // waves waited for all their loads, the A copies from the inbox long
+    // among them): counts the item out of the inbox, item i into counter
+    // i % kGuardCounters, with no returned value. It is issued after the
+    // item's last loads (the last arriver's partials too): a load issued
+    // after it would wait for it. Counting right after the copies, mid-item,
+    // cost 2 us per launch that way.
+    auto count_out = [&]() {
+      if constexpr (GATED) {
+        if (g.consumed != nullptr)
+          __hip_atomic_fetch_add(g.consumed + (item % kGuardCounters) * kGuardStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+
     // Sum the four waves' partials (in wave order), one row at a time.
     float* ws_r = sa.ws + (int64_t)r * M * N;
 #pragma unroll
@@ -267,16 +282,7 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(SmallMArgs sa) {
     if (tid == 0) {
       const uint32_t old = __hip_atomic_fetch_add(sa.counters + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (old == (uint32_t)(R - 1));
-      // Inbox guard: every wave of the item has waited for all its loads
-      // above, the A copies from the inbox long among them; count the item
-      // out of the inbox (item i into counter i % kGuardCounters; no returned
-      // value). Counting right after the copies instead, mid-item, put the
-      // atomic in front of the stream's load waits and cost 2 us per launch.
-      if constexpr (GATED) {
-        if (g.consumed != nullptr)
-          __hip_atomic_fetch_add(g.consumed + (item % kGuardCounters) * kGuardStride, 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (!s_last) count_out();
     }
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(s_last)) continue;
@@ -296,10 +302,12 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(SmallMArgs sa) {
         else static_cast<_Float16*>(g.C)[(int64_t)m * N + col] = (_Float16)v;
       }
     }
-    if (tid == 0) __hip_atomic_store(sa.counters + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(sa.counters + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      count_out();
+    }
     __syncthreads();  // s_last and lds_r are reused by the next item
   }
-  __builtin_amdgcn_s_waitcnt(0);
 }
 
 int mt_of(int64_t M) {
