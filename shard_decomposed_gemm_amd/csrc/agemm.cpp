@@ -67,6 +67,11 @@ struct agemm_ctx {
   uint32_t* guard_mem = nullptr;  // both inboxes' counters, kGuardStride apart
   uint32_t* consumed[2] = {nullptr, nullptr};
   uint32_t guard_target[2][kGuardCounters] = {};
+  uint32_t* go[2] = {nullptr, nullptr};  // each inbox's producer word (its own 4 KiB)
+  uint32_t produce_seq[2] = {0, 0};      // producer launches per inbox so far
+  // Long consumers (M above kGuardOnlyMaxM): the producer also waits, with a
+  // stream dependency, for the last fused consumer of its inbox (see produce).
+  bool producer_waits_event = false;
 
   hipStream_t pair[2] = {nullptr, nullptr};  // agemm_streams: producer, consumer (owned)
   uint64_t* probe_times = nullptr;           // 3 words in ctrl for the overlap probe
@@ -200,6 +205,16 @@ const char* agemm_last_error(const agemm_ctx* ctx) {
   return ctx->last_error.c_str();
 }
 
+// Up to this M the producer of an inbox waits for its earlier fused consumers
+// only on the device (the inbox guard), dispatched as soon as the previous
+// producer is done. Above it, it also waits for the last of them with a
+// stream dependency: a producer dispatched early sits on the CUs through the
+// whole of a long consumer launch, which slowed that launch (fused step, same
+// box, guard only / with the dependency: M = 128 100.6 / 103.6 us; M = 512
+// 227.4 / 225.1 and 223.3 / 223.8 us; M = 4096 1528.9 / 1514.2 us), while the
+// dependency costs a few microseconds of command-processor time per step.
+constexpr int64_t kGuardOnlyMaxM = 256;
+
 int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype, int64_t flag_ktile) {
   if (!out) return AGEMM_EINVAL;
   *out = nullptr;
@@ -280,7 +295,7 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   const size_t inbox_bytes = sizeof(_Float16) * (size_t)W * (size_t)M * (size_t)KS;
   const size_t gathered_bytes = sizeof(_Float16) * (size_t)M * (size_t)K;
   const size_t ctrl_bytes = sizeof(uint32_t) * 2 * kMaxTiles + 8 * sizeof(uint64_t);  // + probe times
-  const size_t guard_bytes = sizeof(uint32_t) * 2 * kGuardCounters * kGuardStride;
+  const size_t guard_bytes = sizeof(uint32_t) * 2 * (kGuardCounters + 1) * kGuardStride;  // + the two words
   int small_max = small_m_default_max();
   if (const char* env = std::getenv("AGEMM_SMALL_M_MAX")) {
     const int v = std::atoi(env);
@@ -331,6 +346,9 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   c->probe_times = c->t0_bsp + 2;
   c->consumed[0] = c->guard_mem;
   c->consumed[1] = c->guard_mem + kGuardCounters * kGuardStride;
+  c->go[0] = c->guard_mem + 2 * kGuardCounters * kGuardStride;
+  c->go[1] = c->go[0] + kGuardStride;
+  c->producer_waits_event = M > kGuardOnlyMaxM;
   void* hp = nullptr;
   e = hipMemset(c->ctrl, 0, ctrl_bytes);
   if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);
@@ -352,6 +370,10 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
       for (int j = 0; j < 2 * kGuardCounters; ++j) {
         counts[(size_t)j * kGuardStride] = base;
         c->guard_target[j / kGuardCounters][j % kGuardCounters] = base;
+      }
+      for (int i = 0; i < 2; ++i) {
+        counts[(size_t)(2 * kGuardCounters + i) * kGuardStride] = base;
+        c->produce_seq[i] = base;
       }
       e = hipMemcpy(c->guard_mem, counts.data(), guard_bytes, hipMemcpyHostToDevice);
     }
@@ -492,11 +514,13 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   // producer waits for them on the device (the inbox guard), not behind a
   // stream dependency. Producers run in call order.
   const int slot = (int)((ctx->epoch + 1) & 1u);
-  hipError_t e = ctx->so.before_produce(s);
+  hipError_t e = ctx->so.before_produce(s, ctx->producer_waits_event ? slot : -1);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
   base_produce_args(ctx, a_shards, pa);
   pa.consumed = ctx->consumed[slot];
   std::memcpy(pa.guard_target, ctx->guard_target[slot], sizeof pa.guard_target);  // wrap with the counters
+  pa.go = ctx->go[slot];
+  pa.go_seq = ctx->produce_seq[slot] + 1u;
   pa.timeout_ticks = ctx->timeout_ticks;
   pa.err = ctx->err_dev;
   pa.dst = ctx->inbox[slot];
@@ -512,6 +536,7 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   ctx->epoch++;
   ctx->slot_epochs[slot]++;
+  ctx->produce_seq[slot]++;
   return AGEMM_OK;
 }
 
@@ -535,7 +560,8 @@ int agemm_run_fused(agemm_ctx* ctx, const void* B, void* C, void* stream) {
   gate.strict = ctx->strict_acquire;
   rc = launch_gemm(ctx, src, gate, B, C, s, ctx->consumed[slot], &ctx->guard_target[slot]);
   if (rc) return rc;
-  const hipError_t e = ctx->so.after_consumer(s);
+  hipError_t e = ctx->producer_waits_event ? ctx->so.after_fused(slot, s) : hipSuccess;
+  if (e == hipSuccess) e = ctx->so.after_consumer(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
   return AGEMM_OK;
 }

@@ -141,6 +141,8 @@ struct ProduceArgs {
   // count into it.
   const uint32_t* consumed;
   uint32_t guard_target[kGuardCounters];
+  uint32_t* go;                     // the inbox's word: workgroup 0 sets it to go_seq once the guard holds
+  uint32_t go_seq;                  // producer launches on this inbox so far, this one included (wrapping)
   uint64_t timeout_ticks;           // bound of the guard wait
   ErrWord* err;
 };

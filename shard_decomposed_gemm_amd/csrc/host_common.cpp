@@ -104,13 +104,16 @@ int find_stream_pair(hipStream_t pair[2], uint64_t* probe_times, double ticks_pe
 hipError_t StreamOrder::create() {
   hipError_t e = hipEventCreateWithFlags(&ev_producer, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_consumer, hipEventDisableTiming);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ev_fused[i], hipEventDisableTiming);
   return e;
 }
 
 void StreamOrder::destroy() {
   if (ev_producer) (void)hipEventDestroy(ev_producer);
   if (ev_consumer) (void)hipEventDestroy(ev_consumer);
-  ev_producer = ev_consumer = nullptr;
+  for (int i = 0; i < 2; ++i)
+    if (ev_fused[i]) (void)hipEventDestroy(ev_fused[i]);
+  ev_producer = ev_consumer = ev_fused[0] = ev_fused[1] = nullptr;
 }
 
 // Makes s wait for the last call marked on `from` (recording its event now if
@@ -138,8 +141,20 @@ hipError_t StreamOrder::mark(hipEvent_t ev, hipStream_t s, bool lazy, hipStream_
   return hipSuccess;
 }
 
-hipError_t StreamOrder::before_produce(hipStream_t s) {
-  return wait_for(ev_producer, producer_stream, producer_pending, &producer_recorded, s);
+hipError_t StreamOrder::before_produce(hipStream_t s, int slot) {
+  hipError_t e = hipSuccess;
+  if (slot >= 0 && fused_pending[slot] && fused_stream[slot] != s) e = hipStreamWaitEvent(s, ev_fused[slot], 0);
+  if (e == hipSuccess) e = wait_for(ev_producer, producer_stream, producer_pending, &producer_recorded, s);
+  return e;
+}
+
+hipError_t StreamOrder::after_fused(int slot, hipStream_t s) {
+  const hipError_t e = hipEventRecord(ev_fused[slot], s);
+  if (e == hipSuccess) {
+    fused_pending[slot] = true;
+    fused_stream[slot] = s;
+  }
+  return e;
 }
 
 hipError_t StreamOrder::after_produce(hipStream_t s) {

@@ -39,11 +39,15 @@ int parse_schedule(const agemm_schedule* sched, int T, double ticks_per_ns, int3
 // Ordering between the calls of one context on different streams. Every
 // producer comes after the previous producer, and every consumer call after
 // the previous consumer call of the context, of any kind (they share
-// workspaces). Producers do not wait for consumers here: the inbox guard
-// holds a producer on the device until the fused consumers that read its
-// inbox before are done with it. A wait is skipped when the previous call ran
-// on the waiting stream (in-stream order already holds, and every dependency
-// packet costs command-processor time between kernels).
+// workspaces). The inbox guard holds a producer on the device until the
+// fused consumers that read its inbox before are done with it; a context may
+// also order the producer after the last fused consumer of its inbox with a
+// stream dependency (`after_fused` records that consumer's event at once,
+// `before_produce` waits for it), so that the producer is not dispatched, and
+// does not sit waiting on the CUs, while that consumer runs. A wait is
+// skipped when the earlier call ran on the waiting stream (in-stream order
+// already holds, and every dependency packet costs command-processor time
+// between kernels).
 //
 // Events of calls on the context's own streams (`owned`, the verified pair)
 // are recorded lazily: only when a call on another stream has to wait for
@@ -58,14 +62,22 @@ struct StreamOrder {
   hipStream_t producer_stream = nullptr, consumer_stream = nullptr;
   bool producer_pending = false, consumer_pending = false;
   bool producer_recorded = true, consumer_recorded = true;
+  hipEvent_t ev_fused[2] = {nullptr, nullptr};  // last fused consumer of each inbox (after_fused)
+  hipStream_t fused_stream[2] = {nullptr, nullptr};
+  bool fused_pending[2] = {false, false};
   hipStream_t owned[2] = {nullptr, nullptr};
 
   hipError_t create();
   void destroy();
-  hipError_t before_produce(hipStream_t s);
+  // After the previous producer; with slot >= 0 also after the last fused
+  // consumer of that inbox marked with after_fused.
+  hipError_t before_produce(hipStream_t s, int slot = -1);
   hipError_t after_produce(hipStream_t s);
   hipError_t before_consumer(hipStream_t s);
   hipError_t after_consumer(hipStream_t s);
+  // Records the event of a fused consumer of inbox `slot` on s at once (for a
+  // later before_produce of that inbox).
+  hipError_t after_fused(int slot, hipStream_t s);
 
  private:
   bool is_owned(hipStream_t s) const { return s != nullptr && (s == owned[0] || s == owned[1]); }

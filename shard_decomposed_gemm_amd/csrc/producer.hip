@@ -25,14 +25,16 @@
 // shared by all workgroups of the launch; offsets do not decrease with p, so
 // a workgroup never holds a later item behind an earlier one's delay.
 //
-// The inbox is guarded on the device: before its first copy, every workgroup waits until the fused consumers that read this
-// inbox in earlier epochs have counted themselves out of it (wave 0 polls the
-// kGuardCounters counters, one lane each, sleeping long between looks). A
-// consumer wave counts itself out only after its inbox reads have returned,
-// so the stores below cannot overtake them. The wait replaces a stream
-// dependency, whose command-processor work sat between consecutive consumer
-// launches (with the record after each consumer that it waits for, about
-// 3 us per step at M = 1).
+// The inbox is guarded on the device: before its first copy, every workgroup
+// waits until the fused consumers that read this inbox in earlier epochs have
+// counted themselves out of it. Workgroup 0's first wave polls the
+// kGuardCounters counters, one lane each, sleeping long between looks, then
+// raises the launch's word, which the other workgroups watch. A consumer
+// counts a unit out only after that unit's inbox reads have returned, so the
+// stores below cannot overtake them. The wait replaces a stream dependency,
+// whose command-processor work sat between consecutive consumer launches
+// (with the record after each consumer that it waits for, about 3 us per
+// step at M = 1).
 #include "agemm_internal.h"
 
 namespace agemm {
@@ -55,7 +57,7 @@ template <bool FLAGS>
 __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a) {
   const int items = a.t * a.items_per_tile;
   if constexpr (FLAGS) {
-    if (a.consumed != nullptr) {
+    if (a.consumed != nullptr && blockIdx.x == 0) {
       if (threadIdx.x < kGuardCounters) {
         const int j = threadIdx.x;
         const uint32_t target = a.guard_target[j];  // wraps with the counter
@@ -75,7 +77,29 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
             break;
           }
           // about 4 us between looks: the consumers it waits for run for tens
-          // of microseconds, and the looks should not load one memory channel
+          // of microseconds or more
+          __builtin_amdgcn_s_sleep(127);
+        }
+        // lets the launch's other workgroups go (after a timeout too)
+        if (j == 0) __hip_atomic_store(a.go, a.go_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+    } else if (a.consumed != nullptr) {
+      // The other workgroups wait for workgroup 0's word, one look each: with
+      // every workgroup reading all the counters, the looks of a 128-workgroup
+      // producer sitting through a 1.5 ms consumer launch slowed it by 1.5 %.
+      if (threadIdx.x == 0) {
+        const uint64_t start = wall_clock();
+        while (true) {
+          const uint32_t v = __hip_atomic_load(a.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((int32_t)(v - a.go_seq) >= 0) break;
+          if (wall_clock() - start > 2 * a.timeout_ticks) {  // workgroup 0 gives up first
+            __hip_atomic_store(&a.err->tile, (uint32_t)kGuardCounters, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&a.err->target, a.go_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&a.err->seen, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&a.err->code, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            break;
+          }
           __builtin_amdgcn_s_sleep(127);
         }
       }
