@@ -118,7 +118,7 @@ typedef struct {
  * min(256, KS), widened until T <= 64. Allocates the inbox and the flags
  * (zeroed) on the current device. Tuning knobs read from the environment at
  * this call (all optional; invalid values are ignored):
- *   AGEMM_SPIN_TIMEOUT_MS    consumer flag-wait timeout (default 2000 ms)
+ *   AGEMM_SPIN_TIMEOUT_MS    flag-wait and inbox-guard timeout (default 2000 ms)
  *   AGEMM_STRICT_ACQUIRE=1   agent-scope acquire fence after each flag wait
  *   AGEMM_TILE_CONFIG=0..2   MFMA tile configuration, BM x BN (four waves, BK): 0
  *                            256x256 (BK 32), 1 128x128 (BK 64), 2 256x128 (BK 32).
@@ -132,10 +132,12 @@ typedef struct {
  *   AGEMM_SMALL_M_PLAN=l,r,w small-M work split: lanes, K-ranges, workgroups per CU
  *   AGEMM_PRODUCER_ITEM_KIB  bytes of one tile copied by one producer workgroup
  *                            (1..1024, default 16)
- *   AGEMM_EPOCH_BASE=n       testing: both inboxes' epoch counts start at n (flags
- *                            set to match), so that a few calls take the 32-bit
- *                            flag counters across their wrap (n = 2^32 - 3 wraps
- *                            on the third call per inbox); anything but a number
+ *   AGEMM_PRODUCER_WGS=n     workgroups of the persistent producer grid (default
+ *                            half the CUs; at most one per CU)
+ *   AGEMM_EPOCH_BASE=n       testing: both inboxes' epoch counts start at n (flags,
+ *                            inbox guard counters and words set to match), so that
+ *                            a few calls take the 32-bit counters across their wrap
+ *                            (n = 2^32 - 3 wraps on the third call per inbox); anything but a number
  *                            in 0..2^32-1 makes agemm_create return EINVAL */
 int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype,
                  int64_t flag_ktile);

@@ -278,12 +278,14 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   if (const char* env = std::getenv("AGEMM_STRICT_ACQUIRE")) c->strict_acquire = std::atoi(env) != 0;
   // The push producer runs beside the consumer: a persistent grid of half as
   // many workgroups as CUs copies the items in release order instead of one
-  // workgroup per item flooding every CU. AGEMM_PRODUCER_WGS overrides (0 =
-  // one workgroup per item).
+  // workgroup per item flooding every CU. AGEMM_PRODUCER_WGS overrides, up to
+  // one workgroup per CU: the workgroups that wait in the inbox guard must
+  // leave room on the CUs for the consumers they wait for (one producer
+  // workgroup fits beside a CU's consumer workgroups).
   c->producer_wgs = c->num_cus / 2;
   if (const char* env = std::getenv("AGEMM_PRODUCER_WGS")) {
     const int v = std::atoi(env);
-    if (v >= 0 && v <= 65536) c->producer_wgs = v;
+    if (v >= 1) c->producer_wgs = std::min(v, c->num_cus);
   }
   if (const char* env = std::getenv("AGEMM_TILE_CONFIG")) {
     const int v = std::atoi(env);
