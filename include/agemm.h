@@ -66,7 +66,9 @@
  * Work split of the GEMM (fixed at create time). With few output tiles (at
  * most half as many as the GPU's compute units) whole tiles would leave most
  * units idle; the GEMM then deals equal runs of (output tile, shard) units to
- * one workgroup per compute unit (stream-K). A tile whose shards
+ * one workgroup per compute unit (stream-K; with the 256-row tiles on 7/8 of
+ * the units, leaving the rest to the producer, since those split kernels
+ * hold a whole SIMD's registers per wave). A tile whose shards
  * fall to several workgroups is summed by the last of them to finish, in a
  * fixed order (contributors' shard ranges ascending), from fp32 partials the
  * others leave in the context's workspace; the result does not depend on

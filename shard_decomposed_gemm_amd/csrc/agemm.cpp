@@ -350,7 +350,10 @@ int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_
   c->consumed[1] = c->guard_mem + kGuardCounters * kGuardStride;
   c->go[0] = c->guard_mem + 2 * kGuardCounters * kGuardStride;
   c->go[1] = c->go[0] + kGuardStride;
-  c->producer_waits_event = M > kGuardOnlyMaxM;
+  // Also where the consumer leaves no room beside it for producer waves (the
+  // split kernels of the 256-row tiles): a producer dispatched early could
+  // then hold CUs that the consumer it waits for still needs.
+  c->producer_waits_event = M > kGuardOnlyMaxM || (!small && c->mplan.split && c->mplan.cfg != 1);
   void* hp = nullptr;
   e = hipMemset(c->ctrl, 0, ctrl_bytes);
   if (e == hipSuccess) e = hipHostMalloc(&hp, sizeof(ErrWord), hipHostMallocMapped | hipHostMallocCoherent);

@@ -849,7 +849,12 @@ MfmaPlan mfma_plan(int64_t M, int64_t N, int64_t K, int W, int num_cus, int tile
   const int64_t g_tiles = std::min<int64_t>(p.tiles, num_cus);
   const int64_t run_tiles = (p.tiles + g_tiles - 1) / g_tiles * W;
   const int64_t units = p.tiles * W;
-  const int64_t g_units = std::min<int64_t>(units, num_cus);
+  // The split kernels of the 256-row tiles hold (nearly) all of a SIMD's 512
+  // registers per wave (their hand-off epilogue), so no producer wave fits on
+  // a CU that runs one: their grid leaves an eighth of the CUs free for the
+  // producer a gated launch waits for.
+  const int64_t split_cus = p.cfg == 1 ? num_cus : std::max<int64_t>(1, num_cus - num_cus / 8);
+  const int64_t g_units = std::min<int64_t>(units, split_cus);
   const int64_t run_units = (units + g_units - 1) / g_units;
   const int64_t saved_columns = (run_tiles - run_units) * (K / W);
   if (split_mode < 0)

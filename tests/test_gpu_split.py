@@ -59,7 +59,8 @@ def test_plan(M, N, K, split):
     assert ctx.split is split
     info = ctx.consumer_info()
     tiles = -(-M // info["block_m"]) * -(-N // info["block_n"])
-    assert ctx.grid == (min(n_cu, tiles * 8) if split else min(n_cu, tiles))
+    split_cus = n_cu if info["tile_config"] == 1 else n_cu - n_cu // 8
+    assert ctx.grid == (min(split_cus, tiles * 8) if split else min(n_cu, tiles))
     ctx.close()
 
 

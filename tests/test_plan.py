@@ -28,6 +28,8 @@ def _default_cfg(M):
     (4096, 28672, 0, 256, False),  # prefill workload: 1792 tiles, 7 per CU
     (128, 4096, 1, 256, True),     # 32 tiles: split over one workgroup per CU
     (512, 2048, 0, 128, True),     # 16 tiles x 8 shards = 128 units
+    (512, 8192, 0, 224, True),     # 64 tiles x 8 shards over 7/8 of the CUs: the 256-row split
+                                   # kernel leaves no room beside it for producer waves
     (9, 256, 1, 16, True),         # 2 tiles x 8 shards
 ])
 def test_workload_plans(M, N, cfg, grid, split):
@@ -70,10 +72,12 @@ def test_plan_invariants_over_a_sweep():
         assert cfg == (tc if tc >= 0 else _default_cfg(M))
         t = _tiles(M, N, cfg)
         if split:
-            assert W >= 2 and grid == min(t * W, cus)
+            # the 256-row tiles' split kernels leave an eighth of the CUs to the producer
+            assert W >= 2 and grid == min(t * W, cus if cfg == 1 else max(1, cus - cus // 8))
             if mode == -1:  # automatic: half of the CUs idle and 4096 columns of K saved
                 run_tiles = -(-t // min(t, cus)) * W
-                run_units = -(-(t * W) // min(t * W, cus))
+                scus = cus if cfg == 1 else max(1, cus - cus // 8)
+                run_units = -(-(t * W) // min(t * W, scus))
                 assert 2 * t <= cus and (run_tiles - run_units) * KS >= 4096
         else:
             assert grid == min(t, cus)
