@@ -210,10 +210,11 @@ int agemm_consumer_grid(const agemm_ctx* ctx, int32_t* grid, int32_t* split);
  * itself out of it, so a producer may fill its inbox while the previous
  * epoch's consumer runs. That run_fused must be able to run meanwhile: on a
  * stream the caller holds up for longer than the spin timeout, the producer
- * gives up waiting (AGEMM_ETIMEOUT from agemm_check). For M above 256 the
- * producer's stream also waits for the last run_fused on its inbox (an event
- * recorded after each run_fused), so that the producer is not dispatched
- * while that long consumer runs. */
+ * gives up waiting (AGEMM_ETIMEOUT from agemm_check). For M above 1024, and
+ * for the stream-K split of the 256-row tiles (which leaves no room for
+ * producer waves beside it), the producer's stream also waits for the last
+ * run_fused on its inbox (an event recorded after each run_fused), so that
+ * the producer is not dispatched while that consumer runs. */
 int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_schedule* sched, void* stream);
 
 /* Flag-gated consumer: C = sum_s Inbox(s) . B_s, waiting on Flags(s, kt)

@@ -209,11 +209,13 @@ const char* agemm_last_error(const agemm_ctx* ctx) {
 // only on the device (the inbox guard), dispatched as soon as the previous
 // producer is done. Above it, it also waits for the last of them with a
 // stream dependency: a producer dispatched early sits on the CUs through the
-// whole of a long consumer launch, which slowed that launch (fused step, same
-// box, guard only / with the dependency: M = 128 100.6 / 103.6 us; M = 512
-// 227.4 / 225.1 and 223.3 / 223.8 us; M = 4096 1528.9 / 1514.2 us), while the
-// dependency costs a few microseconds of command-processor time per step.
-constexpr int64_t kGuardOnlyMaxM = 256;
+// whole of a long consumer launch, which slowed the launches of several
+// rounds of tiles, while the dependency costs a few microseconds of
+// command-processor time per step. Fused step in us, guard alone against
+// guard plus dependency, interleaved on one box each: M = 384 212.4 / 215.2,
+// M = 512 224.7 / 228.1, M = 1024 421.0 / 426.1 and 423.8 / 424.9,
+// M = 2048 838.6 / 821.7, M = 4096 1528.9 / 1514.2.
+constexpr int64_t kGuardOnlyMaxM = 1024;
 
 int agemm_create(agemm_ctx** out, int W, int64_t M, int64_t K, int64_t N, agemm_dtype c_dtype, int64_t flag_ktile) {
   if (!out) return AGEMM_EINVAL;

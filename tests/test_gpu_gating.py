@@ -198,16 +198,16 @@ def test_timeout_reports_and_recovers(M):
     assert np.abs(gu.c_to_f64(C2) - ref).max() <= oracle.tolerance(K)
 
 
-@pytest.mark.parametrize("M,kernel", [(1, "small_m"), (130, "mfma"), (4, "mfma")])
+@pytest.mark.parametrize("M,kernel", [(1, "small_m"), (130, "mfma"), (4, "mfma"), (1040, "mfma")])
 def test_inbox_guard_holds_the_producer_for_a_late_consumer(M, kernel):
-    """The producer waits on the device, not behind a stream dependency, until the
-    fused consumers that read its inbox before are done with it (both consumer
-    kernels count themselves out of the inbox). The consumer of the first epoch
-    starts late (its stream first runs a spin kernel of tens of milliseconds), after
-    the producers of the next two epochs were issued; the third epoch reuses the
-    first one's inbox, so its producer must hold until that consumer has read it
-    (timed: it spans most of the spin). Every epoch's C must equal its own Pull
-    result bit for bit."""
+    """The producer waits on the device until the fused consumers that read its
+    inbox before are done with it (both consumer kernels count themselves out of
+    the inbox); above M = 1024 its stream also waits for the last of them. The
+    consumer of the first epoch starts late (its stream first runs a spin kernel of
+    tens of milliseconds), after the producers of the next two epochs were issued;
+    the third epoch reuses the first one's inbox, so its producer must hold until
+    that consumer has read it (timed: it spans most of the spin). Every epoch's C
+    must equal its own Pull result bit for bit."""
     import torch
     W, K, N = 8, 2048, 1544
     probs = [gu.random_problem(W, M, K, N, seed=s) for s in (71, 72, 73)]
