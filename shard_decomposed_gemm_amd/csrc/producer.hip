@@ -85,9 +85,8 @@ __global__ __launch_bounds__(kProducerThreads) void produce_kernel(ProduceArgs a
       }
       __syncthreads();
     } else if (a.consumed != nullptr) {
-      // The other workgroups wait for workgroup 0's word, one look each: with
-      // every workgroup reading all the counters, the looks of a 128-workgroup
-      // producer sitting through a 1.5 ms consumer launch slowed it by 1.5 %.
+      // The other workgroups wait for workgroup 0's word: one line per look
+      // instead of every workgroup reading all the counters.
       if (threadIdx.x == 0) {
         const uint64_t start = wall_clock();
         while (true) {
