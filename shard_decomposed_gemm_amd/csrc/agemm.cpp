@@ -518,8 +518,9 @@ int agemm_produce(agemm_ctx* ctx, const void* const* a_shards, const agemm_sched
   hipStream_t s = static_cast<hipStream_t>(stream);
   // This epoch's inbox may be overwritten only once the fused consumers that
   // read it before (two epochs ago, and earlier) are done with it: the
-  // producer waits for them on the device (the inbox guard), not behind a
-  // stream dependency. Producers run in call order.
+  // producer waits for them on the device (the inbox guard), and behind a
+  // stream dependency too where producer_waits_event. Producers run in call
+  // order.
   const int slot = (int)((ctx->epoch + 1) & 1u);
   hipError_t e = ctx->so.before_produce(s, ctx->producer_waits_event ? slot : -1);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamWaitEvent");
