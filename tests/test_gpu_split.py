@@ -199,3 +199,37 @@ def test_arrival_order_on_a_split_context_runs_whole_tiles(monkeypatch):
         ctx.check()
         assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), order
     ctx.close()
+
+
+def test_inbox_guard_counts_with_changing_grids():
+    """Fused launches of one context count different numbers of units into the inbox
+    guard: the split (one workgroup per CU) in shard order, whole tiles (32
+    workgroups) in arrival order. Alternating the two over pipelined epochs on the
+    context's stream pair, with no synchronisation between epochs, every producer must
+    find exactly the counts its inbox's earlier launches raise (a total too high
+    would hold it until the spin timeout), and every epoch's C must equal the oracle
+    bit for bit (exact inputs: any summation order gives the same C)."""
+    import torch
+    W, M, K, N = 8, 128, 8192, 4096
+    sets = []
+    for k in range(3):
+        a = gu.coarse_bits(0xFA00 + k, M, K)
+        b = gu.coarse_bits(0xFB00 + k, K, N)
+        sh = synth.shards(a, W)
+        sets.append((oracle.sharded_gemm(sh, b), [gu.to_dev(s) for s in sh], gu.to_dev(b)))
+    ctx = _ctx(W, M, K, N, "f32")
+    assert ctx.split and ctx.consumer_info()["tile_config"] == 1
+    sp, sc = ctx.streams()
+    outs = []
+    for e in range(6):
+        ctx.set_order("arrival" if e % 2 else "shard")
+        ref, dsh, B = sets[e % 3]
+        C = gu.empty_c(M, N, "f32")
+        ctx.produce(dsh, schedule=synth.schedule(0xFC00 + e, ctx.t, 5_000), stream=sp)
+        ctx.run_fused(B, C, stream=sc)
+        outs.append(C)
+    torch.cuda.synchronize()
+    ctx.check()
+    for e, C in enumerate(outs):
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), sets[e % 3][0]), e
+    ctx.close()
