@@ -51,7 +51,8 @@ PEAK_HBM_GBS = 8000.0
 
 
 CSRC = os.path.join(ROOT, "shard_decomposed_gemm_amd", "csrc")
-KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "mfma_sched.h", "agemm_internal.h"), "small_m": ("gemm_small_m.hip", "agemm_internal.h"),
+KERNEL_SOURCES = {"mfma": ("gemm_mfma.hip", "mfma_sched.h", "agemm_internal.h", "guard_units.h"),
+                  "small_m": ("gemm_small_m.hip", "agemm_internal.h", "guard_units.h"),
                   "fd": ("fd_combine.hip", "fd_internal.h", "agemm_internal.h")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "consumer_hbm_traffic.md")
 

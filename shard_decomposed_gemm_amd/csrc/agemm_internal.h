@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "guard_units.h"
+
 namespace agemm {
 
 constexpr int kMaxShards = 16;
@@ -18,17 +20,7 @@ struct ErrWord {
   uint32_t seen;     // last value observed
 };
 
-// Inbox guard: per inbox, kGuardCounters counters into which a fused
-// consumer launch counts its units (the small-M kernel's items, the MFMA
-// kernel's workgroups: unit u into counter u % kGuardCounters) once they are
-// done reading the inbox. The producer of a later epoch on that inbox waits
-// on the device until every counter has reached the total of the launches
-// issued on it, instead of behind a stream dependency. Spreading the counts keeps each address to a few dozen
-// atomics per launch, and one counter per 4 KiB spreads the addresses over
-// the memory channels (counters on a couple of lines serialised the counts
-// and held up the consumer's stream); one wave polls all of them at once.
-constexpr int kGuardCounters = 64;
-constexpr int kGuardStride = 1024;  // uint32 elements from one counter to the next
+// Inbox guard: counters, their spacing and the host's totals (guard_units.h).
 
 // Columns of one k-panel of the inbox layout (see ASource).
 constexpr int kPanelK = 32;
@@ -170,11 +162,7 @@ inline int64_t small_m_guard_units(const SmallMPlan& p) { return (int64_t)p.rang
 // Units an MFMA launch counts into the inbox guard: one per workgroup of the
 // grid launch_gemm_mfma uses for these arguments.
 int64_t mfma_guard_units(const GemmArgs& a);
-// Adds the shares of a launch of `units` units to the guard counters' totals.
-inline void add_guard_units(uint32_t (&target)[kGuardCounters], int64_t units) {
-  for (int j = 0; j < kGuardCounters; ++j)
-    target[j] += (uint32_t)(units / kGuardCounters + (j < units % kGuardCounters ? 1 : 0));
-}
+
 
 // Optional HIP events attached to a consumer kernel's dispatch (its own start
 // and end timestamps); null = plain launch.

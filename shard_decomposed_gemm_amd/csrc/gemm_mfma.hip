@@ -734,7 +734,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs g) {
     if (g.consumed != nullptr) {
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_fetch_add(g.consumed + (int)(blockIdx.x % kGuardCounters) * kGuardStride, 1u, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(g.consumed + guard_counter(blockIdx.x) * kGuardStride, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
   }

@@ -234,15 +234,14 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(SmallMArgs sa) {
 
     // Inbox guard (thread 0, once the workgroup has passed a barrier after its
     // waves waited for all their loads, the A copies from the inbox long
-    // among them): counts the item out of the inbox, item i into counter
-    // i % kGuardCounters, with no returned value. It is issued after the
-    // item's last loads (the last arriver's partials too): a load issued
-    // after it would wait for it. Counting right after the copies, mid-item,
-    // cost 2 us per launch that way.
+    // among them): counts the item out of the inbox, with no returned value.
+    // It is issued after the item's last loads (the last arriver's partials
+    // too): a load issued after it would wait for it. Counting right after
+    // the copies, mid-item, cost 2 us per launch that way.
     auto count_out = [&]() {
       if constexpr (GATED) {
         if (g.consumed != nullptr)
-          __hip_atomic_fetch_add(g.consumed + (item % kGuardCounters) * kGuardStride, 1u, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(g.consumed + guard_counter(item) * kGuardStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
     };
